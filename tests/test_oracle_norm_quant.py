@@ -1,0 +1,190 @@
+"""Pins for the oracle's residual add + RMSNorm + packed-FP8 step.
+
+Closed forms of the RMS normalization, invariants of the block quantization
+(reconstruction error, the amax element maps to code 448, and idempotence:
+requantizing an exactly dequantized packed activation returns the same codes
+and scales, which is the no-unpack-and-requantize contract of the packed
+activation on "[Quant][MTP] Reuse packed FP8 logits inputs", Purpose).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mtp_draft_head_amd import inputs
+
+EPS = 1e-6
+
+
+def bf16_bits(x):
+    return inputs.to_bf16_bits(np.asarray(x, np.float32))
+
+
+def bf16_vals(bits):
+    return torch.from_numpy(np.asarray(bits, np.uint16).view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def dequant_f64(codes, scales):
+    """Exact dequantization with torch's own e4m3fn decode (independent of the oracle's)."""
+    d = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    M, H = codes.shape
+    return (d.reshape(M, H // 128, 128) * scales.astype(np.float64)[:, :, None]).reshape(M, H)
+
+
+def run(h_bits, r_bits, g, eps=EPS):
+    return oracle.norm_quant(h_bits, r_bits, np.asarray(g, np.float32), eps)
+
+
+@pytest.mark.parametrize("c", [1.0, -3.5, 0.001, 37.0, 2.0 ** -20])
+def test_constant_row_closed_form(c):
+    H = 256
+    h = bf16_bits(np.full((1, H), c))
+    r = bf16_bits(np.zeros((1, H)))
+    cv = float(bf16_vals(h)[0, 0])
+    out = run(h, r, np.ones(H))
+    expect = cv / np.sqrt(cv * cv + np.float64(np.float32(EPS)))
+    assert np.allclose(out["y"], expect, rtol=1e-15, atol=0)
+    assert np.all(out["hidden"] == bf16_bits(np.full((1, H), expect))[0, 0])
+    # every element equals the block amax -> every code is +-448, scale = RN_f32(|y|/448)
+    assert np.all((out["codes"] & 0x7F) == 0x7E)
+    assert np.all(out["scales"] == np.float32(abs(expect) / 448.0))
+
+
+def test_zero_row_gives_zero_everything():
+    H = 384
+    z = bf16_bits(np.zeros((2, H)))
+    out = run(z, z, np.ones(H))
+    assert np.all(out["y"] == 0)
+    assert np.all(out["hidden"] == 0)
+    assert np.all(out["codes"] == 0)
+    assert np.all(out["scales"] == 0)
+    assert np.allclose(out["rstd"], 1 / np.sqrt(np.float64(np.float32(EPS))))
+
+
+def test_residual_is_added_and_order_free():
+    rng = np.random.default_rng(1)
+    H = 512
+    a = bf16_bits(rng.standard_normal((3, H)))
+    b = bf16_bits(rng.standard_normal((3, H)))
+    g = rng.uniform(0.5, 1.5, H)
+    o1 = run(a, b, g)
+    o2 = run(b, a, g)
+    assert np.array_equal(o1["y"], o2["y"])
+    # a zero residual leaves the hidden alone: y(h, 0) == y(h + r) when h + r is fed as hidden
+    s = bf16_vals(a) + bf16_vals(b)
+    s_bits = bf16_bits(s)
+    exact = bf16_vals(s_bits) == s                     # rows where the bf16 sum is exact
+    o3 = run(s_bits, bf16_bits(np.zeros((3, H))), g)
+    rows = np.all(exact, axis=1)
+    assert np.allclose(o3["y"][rows], o1["y"][rows], rtol=1e-15, atol=0)
+
+
+def test_unit_rms_before_gain():
+    """mean((y/g)^2) = ms / (ms + eps): the normalized row has unit RMS up to eps."""
+    rng = np.random.default_rng(2)
+    H = 1024
+    h = bf16_bits(rng.standard_normal((8, H)) * rng.uniform(0.01, 10, (8, 1)))
+    r = bf16_bits(rng.standard_normal((8, H)))
+    g = rng.uniform(0.5, 1.5, H).astype(np.float32)
+    out = run(h, r, g)
+    s = bf16_vals(h) + bf16_vals(r)
+    ms = np.mean(s * s, axis=1)
+    lhs = np.mean((out["y"] / g.astype(np.float64)) ** 2, axis=1)
+    assert np.allclose(lhs, ms / (ms + np.float64(np.float32(EPS))), rtol=1e-13)
+    # and the sign of every element follows s
+    assert np.array_equal(np.sign(out["y"]), np.sign(s))
+
+
+def test_linear_in_gain_and_scale_invariant():
+    rng = np.random.default_rng(3)
+    H = 640
+    h = bf16_bits(rng.standard_normal((4, H)))
+    r = bf16_bits(rng.standard_normal((4, H)))
+    g1 = rng.uniform(0.5, 1.5, H).astype(np.float32)
+    g2 = rng.uniform(0.5, 1.5, H).astype(np.float32)
+    gs = (g1.astype(np.float64) + g2).astype(np.float32)
+    ok = gs.astype(np.float64) == g1.astype(np.float64) + g2          # exact sums only
+    y1, y2, ys = run(h, r, g1)["y"], run(h, r, g2)["y"], run(h, r, gs)["y"]
+    assert np.allclose(ys[:, ok], (y1 + y2)[:, ok], rtol=1e-14)
+    # scaling both inputs by 2^k scales s exactly; y moves only through eps
+    h8 = bf16_bits(bf16_vals(h) * 8.0)
+    r8 = bf16_bits(bf16_vals(r) * 8.0)
+    y8 = run(h8, r8, g1)["y"]
+    assert np.allclose(y8, y1, rtol=1e-6)
+
+
+def test_recycled_hidden_is_rne_of_y():
+    rng = np.random.default_rng(4)
+    H = 768
+    out = run(bf16_bits(rng.standard_normal((5, H))), bf16_bits(rng.standard_normal((5, H))),
+              rng.uniform(0.5, 1.5, H))
+    # torch's cast of the fp64 y is not used (it may round twice); instead bracket:
+    # the output is one of the two bf16 neighbours of y and the nearer one.
+    got = bf16_vals(out["hidden"])
+    err = np.abs(got - out["y"])
+    y32 = out["y"].astype(np.float32)
+    lo_bits = torch.from_numpy(y32).to(torch.bfloat16).to(torch.float64).numpy()
+    ulp = np.abs(np.ldexp(1.0, np.frexp(np.abs(got))[1] - 8))
+    assert np.all(err <= ulp / 2 * (1 + 1e-12))
+    assert np.all(np.abs(lo_bits - got) <= ulp)
+
+
+def _quant_invariants(y, codes, scales):
+    M, H = y.shape
+    KB = H // 128
+    dq = dequant_f64(codes, scales)
+    yb = y.reshape(M, KB, 128)
+    s64 = scales.astype(np.float64)
+    amax = np.abs(yb).max(axis=2)
+    # scale is RN_f32(amax / 448)
+    assert np.array_equal(scales, (amax / 448.0).astype(np.float32))
+    nz = scales > 0
+    # (i) reconstruction error: at most half the e4m3 spacing at y/scale, times scale,
+    # plus the fp32 rounding of the quotient the code is decided on
+    q = np.where(nz[:, :, None], yb / np.where(nz, s64, 1.0)[:, :, None], 0.0)
+    aq = np.abs(q)
+    e = np.floor(np.log2(np.maximum(aq, 2.0 ** -6)))
+    spacing = np.ldexp(1.0, (e - 3).astype(int))
+    bound = (spacing / 2 + aq * 2.0 ** -23) * s64[:, :, None]
+    err = np.abs(dq.reshape(M, KB, 128) - yb)
+    assert np.all(err[nz] <= bound[nz] * (1 + 1e-12))
+    # (ii) each nonzero block holds a code of magnitude 448
+    mags = (codes.reshape(M, KB, 128) & 0x7F).max(axis=2)
+    assert np.all(mags[nz] == 0x7E)
+    assert np.all(codes.reshape(M, KB, 128)[~nz] == 0)
+
+
+def test_block_quant_invariants_and_idempotence():
+    rng = np.random.default_rng(5)
+    M, H = 16, 1024
+    y = rng.standard_normal((M, H)) * rng.uniform(1e-3, 50, (M, 1))
+    y[3, 128:256] = 0.0                     # an all-zero block
+    y[4, :128] = 1e-30                      # a block whose scale underflows to 0 in fp32... or not
+    y[5, 7] = 1e4                           # an outlier dominating one block
+    codes, scales = oracle.block_quant(y)
+    _quant_invariants(y, codes, scales)
+    assert np.all(scales[3, 1] == 0) and np.all(codes[3, 128:256] == 0)
+    # (iii) idempotence: requantize the exact dequantization -> identical codes and scales
+    c2, s2 = oracle.block_quant(dequant_f64(codes, scales))
+    assert np.array_equal(s2, scales)
+    assert np.array_equal(c2, codes)
+
+
+def test_idempotence_fails_if_dequant_is_rounded_to_bf16():
+    """Guards the idempotence test: dequantizing through bf16 breaks it."""
+    rng = np.random.default_rng(6)
+    y = rng.standard_normal((8, 512)) * 3
+    codes, scales = oracle.block_quant(y)
+    dq = dequant_f64(codes, scales)
+    dq16 = bf16_vals(bf16_bits(dq))
+    c2, s2 = oracle.block_quant(dq16)
+    assert not (np.array_equal(s2, scales) and np.array_equal(c2, codes))
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_c1_tp8_shard"])
+def test_workload_norm_quant_invariants(name, workloads):
+    d = workloads(name)
+    out = oracle.norm_quant(d["hidden"], d["residual"], d["norm_weight"], d["eps"])
+    _quant_invariants(out["y"], out["codes"], out["scales"])
+    c2, s2 = oracle.block_quant(dequant_f64(out["codes"], out["scales"]))
+    assert np.array_equal(c2, out["codes"]) and np.array_equal(s2, out["scales"])
