@@ -1,0 +1,166 @@
+/*
+ * mtpd.h -- C ABI of libmtpd, the MTP draft-layer tail on one AMD MI355X
+ * (gfx950): residual add + RMSNorm producing a bf16 recycled hidden and a
+ * packed FP8 activation, a block-scaled FP8 LM head over that activation,
+ * and a fused greedy argmax that never writes logits to memory.
+ *
+ * Where the operations are defined:
+ *   - "[Quant][MTP] Reuse packed FP8 logits inputs", Purpose: the MTP layer
+ *     fuses its final all-reduce and RMSNorm with packed FP8 quantization for
+ *     the shared LM head and returns two different values, the packed
+ *     activation for the logits and the post-norm bf16 hidden for the next
+ *     MTP position; consumers index that packed activation and never unpack
+ *     and requantize it.  Dependencies: the LM-head GEMM takes the activation
+ *     prequantized, block-linear.
+ *   - "[Spec Decode][Perf] Fuse the MTP trailing all-reduce; local-argmax
+ *     draft tokens", Summary: greedy draft tokens come from a local argmax
+ *     over this GPU's vocab slice instead of gathering full-vocab logits.
+ *     Accuracy: the fused norm accumulates in fp32.
+ *
+ * Formats (all row-major, all device memory unless stated):
+ *   bf16         uint16 bit patterns of bfloat16.
+ *   E4M3 codes   OCP FP8 E4M3FN (max 448, no infinities, 0x7F/0xFF NaN).
+ *   packed act   codes [rows][cols] u8 and scales [rows][cols/128] f32; the
+ *                value of element (r, c) is dec(code) * scale[r][c/128].
+ *   FP8 weight   codes [V][H] u8 (K contiguous) and scales [V/128][H/128]
+ *                f32, one per 128x128 block.
+ *
+ * Conventions shared by every entry point:
+ *   - The caller owns all memory; the library allocates nothing and keeps no
+ *     state between calls.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     null stream) and never synchronizes.
+ *   - Arguments are validated on the host before any HIP call; on failure
+ *     nothing is launched and a status other than MTPD_OK is returned.  A
+ *     failed launch returns MTPD_ERR_HIP.  Faults inside a kernel surface at
+ *     the caller's next synchronization.
+ *   - The first failure on a thread is kept (mtpd_last_error) until
+ *     mtpd_clear_error is called; later failures do not overwrite it.
+ *   - Inputs are never written.  Outputs must not overlap inputs or each
+ *     other.  Every output element is overwritten.
+ *   - Limits: 128 <= H <= 16384 and H % 128 == 0; V % 128 == 0 and
+ *     128 <= V <= 2^31 - 128; 0 <= M, n_rows <= 2^24.  M == 0 (or
+ *     n_rows == 0) is a valid empty call that launches nothing.
+ *   - Alignment: bf16 arrays, code arrays and norm_weight 16 bytes; scale,
+ *     max and index arrays 4 bytes; workspace 256 bytes.
+ *   - Non-finite inputs give unspecified (but memory-safe) results.
+ */
+#ifndef MTPD_H
+#define MTPD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MTPD_OK = 0,
+    MTPD_ERR_NULL = 1,      /* a required pointer is NULL */
+    MTPD_ERR_SHAPE = 2,     /* a size is out of range or inconsistent */
+    MTPD_ERR_ALIGN = 3,     /* a pointer is not aligned as required */
+    MTPD_ERR_ALIAS = 4,     /* an output overlaps an input or another output */
+    MTPD_ERR_WORKSPACE = 5, /* workspace missing or smaller than mtpd_workspace_bytes */
+    MTPD_ERR_HIP = 6        /* the HIP runtime refused a launch or query */
+} mtpd_status;
+
+/* Packed FP8 activation ("QuantizedActivation"): codes [rows][cols] OCP
+ * E4M3FN, scales [rows][cols/128] fp32 dequant multipliers.  cols % 128 == 0. */
+typedef struct {
+    uint8_t *codes;
+    float *scales;
+    int64_t rows;
+    int64_t cols;
+} mtpd_qact;
+
+/* Shared FP8 LM head (or this GPU's vocab shard of it): codes [V][H] OCP
+ * E4M3FN, K contiguous; scales [V/128][H/128] fp32, one per 128x128 block. */
+typedef struct {
+    const uint8_t *codes;
+    const float *scales;
+    int64_t V;
+    int64_t H;
+} mtpd_fp8_weight;
+
+/*
+ * Residual add + RMSNorm + dual output
+ * ("Reuse packed FP8 logits inputs", Purpose; fp32 accumulation per
+ * "Fuse the MTP trailing all-reduce; local-argmax draft tokens", Accuracy).
+ *
+ *   s = f32(hidden) + f32(residual)                      per element
+ *   rstd = 1 / sqrt(sum(s^2) / H + eps)                  sum accumulated in fp32
+ *   y = s * rstd * norm_weight                           fp32, not rounded
+ *   out_hidden = RNE_bf16(y)                             the recycled hidden
+ *   per 128-column block b of each row:
+ *     scale_b = RN_f32(max|y| / 448)                     dequant multiplier
+ *     code    = E4M3(RN_f32(y / scale_b)), clamped to +-448, ties to even
+ *     (scale_b == 0 gives scale 0 and all codes 0x00)
+ *
+ * hidden, residual: [M][H] bf16.  norm_weight: [H] f32.  eps: added to the
+ * mean square (inside the square root).  out_hidden: [M][H] bf16.  out_act:
+ * rows == M, cols == H; its codes and scales are written.
+ */
+mtpd_status mtpd_norm_quant(const uint16_t *hidden, const uint16_t *residual,
+                            const float *norm_weight, float eps, int64_t M, int64_t H,
+                            uint16_t *out_hidden, const mtpd_qact *out_act, void *stream);
+
+/*
+ * Block-scaled FP8 LM head fused with a greedy local argmax
+ * ("Reuse packed FP8 logits inputs", Purpose and Dependencies;
+ * "Fuse the MTP trailing all-reduce; local-argmax draft tokens", Summary).
+ *
+ * For output row i, with a = row_index ? row_index[i] : i:
+ *   z[v] = sum_b act.scales[a][b] * w.scales[v/128][b] *
+ *          sum_{k in block b} dec(act.codes[a][k]) * dec(w.codes[v][k])
+ *   out_idx[i] = the lowest v in [0, V) attaining the largest fp32 z[v]
+ *                (+0 and -0 compare equal); out_max[i] = that z, in fp32.
+ * The logits z are never written to memory.  out_idx is local to this
+ * weight (a vocab shard's caller adds the shard offset).
+ *
+ * act: rows >= 1, cols == w->H.  row_index: [n_rows] int32 rows of act, or
+ * NULL for rows 0..n_rows-1 (then n_rows <= act->rows); its values must lie
+ * in [0, act->rows) and are not checked on the device.  out_max: [n_rows]
+ * f32.  out_idx: [n_rows] int32.
+ * workspace: device memory of at least mtpd_workspace_bytes(n_rows) bytes,
+ * ZERO-FILLED before its first use; every call that runs to completion
+ * leaves it zero-filled again.  Calls that share a workspace must not
+ * overlap in time; after a call that did not complete, zero it again.
+ */
+mtpd_status mtpd_fp8_lmhead_argmax(const mtpd_qact *act, const int32_t *row_index, int64_t n_rows,
+                                   const mtpd_fp8_weight *w, float *out_max, int32_t *out_idx,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The whole draft tail for M rows: mtpd_norm_quant followed by
+ * mtpd_fp8_lmhead_argmax on every row of the packed activation it produced
+ * (row_index NULL).  Same arguments, layouts, workspace contract and
+ * results as the two calls in sequence; w->H must equal H.
+ */
+mtpd_status mtpd_draft_tail(const uint16_t *hidden, const uint16_t *residual,
+                            const float *norm_weight, float eps, int64_t M, int64_t H,
+                            const mtpd_fp8_weight *w, uint16_t *out_hidden, const mtpd_qact *out_act,
+                            float *out_max, int32_t *out_idx,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace mtpd_fp8_lmhead_argmax / mtpd_draft_tail need for
+ * n_rows output rows (a multiple of 256; 0 for n_rows <= 0). */
+size_t mtpd_workspace_bytes(int64_t n_rows);
+
+/* Static name of a status code ("MTPD_OK", ...); "MTPD_UNKNOWN" otherwise. */
+const char *mtpd_status_name(mtpd_status s);
+
+/* Detail of the first failure on the calling thread since the last
+ * mtpd_clear_error (empty string if none).  The pointer stays valid until
+ * the next mtpd_clear_error on this thread. */
+const char *mtpd_last_error(void);
+void mtpd_clear_error(void);
+
+/* ABI version: bumped when any declaration above changes. */
+int mtpd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTPD_H */

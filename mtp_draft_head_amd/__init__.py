@@ -1,0 +1,250 @@
+"""MTP draft-layer tail on one AMD MI355X (gfx950).
+
+Thin Python binding over libmtpd's C ABI (``include/mtpd.h``): it checks
+tensor dtypes, devices and contiguity, then passes raw device pointers and
+the current HIP stream.  Every step of the path runs in the HIP kernels of
+libmtpd; this module only marshals arguments.  PyTorch supplies device memory
+and streams.
+
+The library is loaded on first use from ``mtp_draft_head_amd/_build``; if it
+is missing, calls raise ``MtpdLibraryMissing`` -- there is no fallback.
+Build it with ``python -m mtp_draft_head_amd.build`` (or the repository's
+``__graft_entry__.build()``).
+
+Entry points (same names as the C ABI):
+  norm_quant(hidden, residual, norm_weight, eps)
+      -> (out_hidden bf16 [M,H], codes uint8 [M,H], scales f32 [M,H/128])
+  fp8_lmhead_argmax(codes, scales, w_codes, w_scales, row_index=None)
+      -> (max f32 [n], idx int32 [n])
+  draft_tail(hidden, residual, norm_weight, eps, w_codes, w_scales)
+      -> (out_hidden, codes, scales, max, idx)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "MtpdError", "MtpdLibraryMissing", "norm_quant", "fp8_lmhead_argmax", "draft_tail",
+    "workspace_bytes", "Workspace", "library_path", "lib",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+BLOCK = 128
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "_build", "libmtpd.so")
+
+
+class MtpdLibraryMissing(RuntimeError):
+    pass
+
+
+class MtpdError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name} ({status}): {detail}")
+        self.status = status
+        self.name = name
+        self.detail = detail
+
+
+class QAct(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class FP8Weight(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("V", ctypes.c_int64), ("H", ctypes.c_int64)]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib():
+    """The loaded libmtpd (ctypes.CDLL), with argument types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise MtpdLibraryMissing(
+                f"{path} is not built; run `python -m mtp_draft_head_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(path)
+        P, I64, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+        L.mtpd_norm_quant.restype = ctypes.c_int
+        L.mtpd_norm_quant.argtypes = [P, P, P, F, I64, I64, P, ctypes.POINTER(QAct), P]
+        L.mtpd_fp8_lmhead_argmax.restype = ctypes.c_int
+        L.mtpd_fp8_lmhead_argmax.argtypes = [ctypes.POINTER(QAct), P, I64, ctypes.POINTER(FP8Weight),
+                                             P, P, P, ctypes.c_size_t, P]
+        L.mtpd_draft_tail.restype = ctypes.c_int
+        L.mtpd_draft_tail.argtypes = [P, P, P, F, I64, I64, ctypes.POINTER(FP8Weight), P,
+                                      ctypes.POINTER(QAct), P, P, P, ctypes.c_size_t, P]
+        L.mtpd_workspace_bytes.restype = ctypes.c_size_t
+        L.mtpd_workspace_bytes.argtypes = [I64]
+        L.mtpd_status_name.restype = ctypes.c_char_p
+        L.mtpd_status_name.argtypes = [ctypes.c_int]
+        L.mtpd_last_error.restype = ctypes.c_char_p
+        L.mtpd_last_error.argtypes = []
+        L.mtpd_clear_error.restype = None
+        L.mtpd_clear_error.argtypes = []
+        L.mtpd_abi_version.restype = ctypes.c_int
+        L.mtpd_abi_version.argtypes = []
+        _lib = L
+        return L
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        name = L.mtpd_status_name(status).decode()
+        detail = L.mtpd_last_error().decode()
+        L.mtpd_clear_error()
+        raise MtpdError(status, name, detail)
+
+
+def workspace_bytes(n_rows: int) -> int:
+    return int(lib().mtpd_workspace_bytes(int(n_rows)))
+
+
+class Workspace:
+    """A zero-filled device workspace, grown on demand and reused.
+
+    The library leaves the workspace zero-filled after every completed call,
+    so one buffer serves any number of calls issued in order on one stream.
+    """
+
+    def __init__(self, device=None):
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.buf = None
+
+    def get(self, n_rows: int) -> torch.Tensor:
+        need = workspace_bytes(n_rows)
+        if self.buf is None or self.buf.numel() < need:
+            self.buf = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+_default_ws: dict = {}
+
+
+def _workspace_for(device: torch.device) -> Workspace:
+    key = (device.type, device.index)
+    if key not in _default_ws:
+        _default_ws[key] = Workspace(device)
+    return _default_ws[key]
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, dim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device}); there is no CPU path")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != dim:
+        raise ValueError(f"{name} must be {dim}-D, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_U8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _weight(w_codes, w_scales) -> FP8Weight:
+    _dev(w_codes, "w_codes", _U8, 2)
+    _dev(w_scales, "w_scales", (torch.float32,), 2)
+    V, H = w_codes.shape
+    return FP8Weight(w_codes.data_ptr(), w_scales.data_ptr(), V, H)
+
+
+def norm_quant(hidden, residual, norm_weight, eps: float = 1e-6, out=None):
+    """Residual add + RMSNorm -> (bf16 recycled hidden, E4M3 codes, fp32 block scales)."""
+    _dev(hidden, "hidden", _BF16, 2)
+    _dev(residual, "residual", _BF16, 2)
+    _dev(norm_weight, "norm_weight", (torch.float32,), 1)
+    M, H = hidden.shape
+    dev = hidden.device
+    if out is None:
+        out_h = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        codes = torch.empty((M, H), dtype=torch.uint8, device=dev)
+        scales = torch.empty((M, H // BLOCK if H % BLOCK == 0 else 0), dtype=torch.float32, device=dev)
+    else:
+        out_h, codes, scales = out
+    qa = QAct(codes.data_ptr(), scales.data_ptr(), M, H)
+    with torch.cuda.device(dev):
+        _check(lib().mtpd_norm_quant(hidden.data_ptr(), residual.data_ptr(), norm_weight.data_ptr(),
+                                     float(eps), M, H, out_h.data_ptr(), ctypes.byref(qa), _stream(dev)))
+    return out_h, codes, scales
+
+
+def fp8_lmhead_argmax(codes, scales, w_codes, w_scales, row_index=None, workspace: Workspace | None = None,
+                      out=None):
+    """Greedy local argmax of the block-scaled FP8 LM head over a packed activation.
+
+    Returns (max float32 [n], idx int32 [n]); idx is local to this weight.
+    row_index (int32 [n]) selects activation rows; None means all rows.
+    """
+    _dev(codes, "codes", _U8, 2)
+    _dev(scales, "scales", (torch.float32,), 2)
+    w = _weight(w_codes, w_scales)
+    dev = codes.device
+    A, H = codes.shape
+    if row_index is not None:
+        _dev(row_index, "row_index", (torch.int32,), 1)
+        n = row_index.shape[0]
+        ri = row_index.data_ptr()
+    else:
+        n, ri = A, None
+    if out is None:
+        out_max = torch.empty((n,), dtype=torch.float32, device=dev)
+        out_idx = torch.empty((n,), dtype=torch.int32, device=dev)
+    else:
+        out_max, out_idx = out
+    ws = (workspace or _workspace_for(dev)).get(n)
+    qa = QAct(codes.data_ptr(), scales.data_ptr(), A, H)
+    with torch.cuda.device(dev):
+        _check(lib().mtpd_fp8_lmhead_argmax(ctypes.byref(qa), ri, n, ctypes.byref(w), out_max.data_ptr(),
+                                            out_idx.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
+    return out_max, out_idx
+
+
+def draft_tail(hidden, residual, norm_weight, eps, w_codes, w_scales, workspace: Workspace | None = None,
+               out=None):
+    """The whole tail: (out_hidden, codes, scales, max, idx) for every row."""
+    _dev(hidden, "hidden", _BF16, 2)
+    _dev(residual, "residual", _BF16, 2)
+    _dev(norm_weight, "norm_weight", (torch.float32,), 1)
+    w = _weight(w_codes, w_scales)
+    M, H = hidden.shape
+    dev = hidden.device
+    if out is None:
+        out_h = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        codes = torch.empty((M, H), dtype=torch.uint8, device=dev)
+        scales = torch.empty((M, H // BLOCK if H % BLOCK == 0 else 0), dtype=torch.float32, device=dev)
+        out_max = torch.empty((M,), dtype=torch.float32, device=dev)
+        out_idx = torch.empty((M,), dtype=torch.int32, device=dev)
+    else:
+        out_h, codes, scales, out_max, out_idx = out
+    ws = (workspace or _workspace_for(dev)).get(M)
+    qa = QAct(codes.data_ptr(), scales.data_ptr(), M, H)
+    with torch.cuda.device(dev):
+        _check(lib().mtpd_draft_tail(hidden.data_ptr(), residual.data_ptr(), norm_weight.data_ptr(), float(eps),
+                                     M, H, ctypes.byref(w), out_h.data_ptr(), ctypes.byref(qa),
+                                     out_max.data_ptr(), out_idx.data_ptr(), ws.data_ptr(), ws.numel(),
+                                     _stream(dev)))
+    return out_h, codes, scales, out_max, out_idx

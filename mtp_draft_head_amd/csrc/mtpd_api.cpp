@@ -1,0 +1,227 @@
+// C ABI of libmtpd: argument validation, error reporting and dispatch.
+// Every argument is checked before the first HIP call, so an invalid call
+// launches nothing and touches no device state.
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kernels.h"
+#include "mtpd.h"
+
+namespace {
+
+thread_local char g_err[512] = {0};
+
+mtpd_status fail(mtpd_status st, const char* fmt, ...) {
+    if (g_err[0] == 0) {   // the first failure is the root cause; keep it
+        int n = snprintf(g_err, sizeof g_err, "%s: ", mtpd_status_name(st));
+        if (n < 0) n = 0;
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(g_err + n, sizeof g_err - (size_t)n, fmt, ap);
+        va_end(ap);
+    }
+    return st;
+}
+
+constexpr int64_t kMaxH = 16384;
+constexpr int64_t kMaxV = 0x7FFFFF80LL;   // 2^31 - 128
+constexpr int64_t kMaxRows = 1LL << 24;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Range {
+    const void* p;
+    size_t bytes;
+    const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) {
+    if (!a.bytes || !b.bytes) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// outputs must not overlap each other nor any input
+mtpd_status check_alias(const Range* outs, int n_out, const Range* ins, int n_in) {
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlap(outs[i], outs[j]))
+                return fail(MTPD_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+        for (int j = 0; j < n_in; ++j)
+            if (overlap(outs[i], ins[j]))
+                return fail(MTPD_ERR_ALIAS, "%s overlaps input %s", outs[i].name, ins[j].name);
+    }
+    return MTPD_OK;
+}
+
+mtpd_status check_H(int64_t H) {
+    if (H < mtpd::kBlock || H > kMaxH || H % mtpd::kBlock)
+        return fail(MTPD_ERR_SHAPE, "H=%lld must be a multiple of 128 in [128, %lld]", (long long)H,
+                    (long long)kMaxH);
+    return MTPD_OK;
+}
+
+mtpd_status check_weight(const mtpd_fp8_weight* w, int64_t H) {
+    if (!w) return fail(MTPD_ERR_NULL, "weight descriptor is NULL");
+    if (!w->codes || !w->scales) return fail(MTPD_ERR_NULL, "weight codes/scales pointer is NULL");
+    if (w->H != H) return fail(MTPD_ERR_SHAPE, "weight H=%lld differs from H=%lld", (long long)w->H, (long long)H);
+    if (w->V < mtpd::kBlock || w->V > kMaxV || w->V % mtpd::kBlock)
+        return fail(MTPD_ERR_SHAPE, "V=%lld must be a multiple of 128 in [128, 2^31-128]", (long long)w->V);
+    if (!aligned(w->codes, 16)) return fail(MTPD_ERR_ALIGN, "weight codes not 16-byte aligned");
+    if (!aligned(w->scales, 4)) return fail(MTPD_ERR_ALIGN, "weight scales not 4-byte aligned");
+    return MTPD_OK;
+}
+
+mtpd_status check_norm_args(const uint16_t* hidden, const uint16_t* residual, const float* norm_weight,
+                            int64_t M, int64_t H, const uint16_t* out_hidden, const mtpd_qact* out_act) {
+    if (M < 0 || M > kMaxRows) return fail(MTPD_ERR_SHAPE, "M=%lld out of [0, 2^24]", (long long)M);
+    mtpd_status st = check_H(H);
+    if (st != MTPD_OK) return st;
+    if (!out_act) return fail(MTPD_ERR_NULL, "out_act descriptor is NULL");
+    if (out_act->rows != M || out_act->cols != H)
+        return fail(MTPD_ERR_SHAPE, "out_act is [%lld x %lld], expected [%lld x %lld]", (long long)out_act->rows,
+                    (long long)out_act->cols, (long long)M, (long long)H);
+    if (M == 0) return MTPD_OK;
+    if (!hidden || !residual || !norm_weight || !out_hidden || !out_act->codes || !out_act->scales)
+        return fail(MTPD_ERR_NULL, "a required pointer is NULL");
+    if (!aligned(hidden, 16) || !aligned(residual, 16) || !aligned(out_hidden, 16) ||
+        !aligned(out_act->codes, 16) || !aligned(norm_weight, 16))
+        return fail(MTPD_ERR_ALIGN, "bf16/code/norm-weight arrays must be 16-byte aligned");
+    if (!aligned(out_act->scales, 4)) return fail(MTPD_ERR_ALIGN, "scales not 4-byte aligned");
+    return MTPD_OK;
+}
+
+mtpd_status check_lmhead_outputs(int64_t n_rows, const float* out_max, const int32_t* out_idx,
+                                 const void* workspace, size_t workspace_bytes) {
+    if (!out_max || !out_idx) return fail(MTPD_ERR_NULL, "out_max/out_idx is NULL");
+    if (!aligned(out_max, 4) || !aligned(out_idx, 4)) return fail(MTPD_ERR_ALIGN, "out_max/out_idx not 4-byte aligned");
+    const size_t need = mtpd::workspace_bytes(n_rows);
+    if (!workspace || workspace_bytes < need)
+        return fail(MTPD_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", workspace_bytes, workspace,
+                    need);
+    if (!aligned(workspace, 256)) return fail(MTPD_ERR_ALIGN, "workspace not 256-byte aligned");
+    return MTPD_OK;
+}
+
+mtpd_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return MTPD_OK;
+    return fail(MTPD_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mtpd_status_name(mtpd_status s) {
+    switch (s) {
+        case MTPD_OK: return "MTPD_OK";
+        case MTPD_ERR_NULL: return "MTPD_ERR_NULL";
+        case MTPD_ERR_SHAPE: return "MTPD_ERR_SHAPE";
+        case MTPD_ERR_ALIGN: return "MTPD_ERR_ALIGN";
+        case MTPD_ERR_ALIAS: return "MTPD_ERR_ALIAS";
+        case MTPD_ERR_WORKSPACE: return "MTPD_ERR_WORKSPACE";
+        case MTPD_ERR_HIP: return "MTPD_ERR_HIP";
+    }
+    return "MTPD_UNKNOWN";
+}
+
+const char* mtpd_last_error(void) { return g_err; }
+
+void mtpd_clear_error(void) { g_err[0] = 0; }
+
+int mtpd_abi_version(void) { return 1; }
+
+size_t mtpd_workspace_bytes(int64_t n_rows) { return mtpd::workspace_bytes(n_rows); }
+
+mtpd_status mtpd_norm_quant(const uint16_t* hidden, const uint16_t* residual, const float* norm_weight, float eps,
+                            int64_t M, int64_t H, uint16_t* out_hidden, const mtpd_qact* out_act, void* stream) {
+    mtpd_status st = check_norm_args(hidden, residual, norm_weight, M, H, out_hidden, out_act);
+    if (st != MTPD_OK || M == 0) return st;
+    const size_t mh = (size_t)M * (size_t)H;
+    const Range outs[] = {{out_hidden, mh * 2, "out_hidden"},
+                          {out_act->codes, mh, "out_act.codes"},
+                          {out_act->scales, mh / 128 * 4, "out_act.scales"}};
+    const Range ins[] = {{hidden, mh * 2, "hidden"}, {residual, mh * 2, "residual"}, {norm_weight, (size_t)H * 4, "norm_weight"}};
+    st = check_alias(outs, 3, ins, 3);
+    if (st != MTPD_OK) return st;
+    return hip_status(mtpd::launch_norm_quant(hidden, residual, norm_weight, eps, M, H, out_hidden, out_act->codes,
+                                              out_act->scales, (hipStream_t)stream),
+                      "norm_quant launch");
+}
+
+mtpd_status mtpd_fp8_lmhead_argmax(const mtpd_qact* act, const int32_t* row_index, int64_t n_rows,
+                                   const mtpd_fp8_weight* w, float* out_max, int32_t* out_idx, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (!act) return fail(MTPD_ERR_NULL, "act descriptor is NULL");
+    if (n_rows < 0 || n_rows > kMaxRows) return fail(MTPD_ERR_SHAPE, "n_rows=%lld out of [0, 2^24]", (long long)n_rows);
+    mtpd_status st = check_H(act->cols);
+    if (st != MTPD_OK) return st;
+    st = check_weight(w, act->cols);
+    if (st != MTPD_OK) return st;
+    if (n_rows == 0) return MTPD_OK;
+    if (act->rows < 1 || act->rows > kMaxRows)
+        return fail(MTPD_ERR_SHAPE, "act rows=%lld out of [1, 2^24]", (long long)act->rows);
+    if (!row_index && n_rows > act->rows)
+        return fail(MTPD_ERR_SHAPE, "n_rows=%lld exceeds act rows=%lld with no row_index", (long long)n_rows,
+                    (long long)act->rows);
+    if (!act->codes || !act->scales) return fail(MTPD_ERR_NULL, "act codes/scales pointer is NULL");
+    if (!aligned(act->codes, 16)) return fail(MTPD_ERR_ALIGN, "act codes not 16-byte aligned");
+    if (!aligned(act->scales, 4)) return fail(MTPD_ERR_ALIGN, "act scales not 4-byte aligned");
+    if (row_index && !aligned(row_index, 4)) return fail(MTPD_ERR_ALIGN, "row_index not 4-byte aligned");
+    st = check_lmhead_outputs(n_rows, out_max, out_idx, workspace, workspace_bytes);
+    if (st != MTPD_OK) return st;
+    const size_t ah = (size_t)act->rows * (size_t)act->cols;
+    const Range outs[] = {{out_max, (size_t)n_rows * 4, "out_max"},
+                          {out_idx, (size_t)n_rows * 4, "out_idx"},
+                          {workspace, mtpd::workspace_bytes(n_rows), "workspace"}};
+    const Range ins[] = {{act->codes, ah, "act.codes"},
+                         {act->scales, ah / 128 * 4, "act.scales"},
+                         {row_index, row_index ? (size_t)n_rows * 4 : 0, "row_index"},
+                         {w->codes, (size_t)w->V * (size_t)w->H, "w.codes"},
+                         {w->scales, (size_t)(w->V / 128) * (size_t)(w->H / 128) * 4, "w.scales"}};
+    st = check_alias(outs, 3, ins, 5);
+    if (st != MTPD_OK) return st;
+    mtpd::LmheadArgs a{act->codes, act->scales, row_index, n_rows, w->codes, w->scales, w->V, w->H,
+                       out_max, out_idx, workspace};
+    return hip_status(mtpd::launch_lmhead_argmax(a, (hipStream_t)stream), "lmhead_argmax launch");
+}
+
+mtpd_status mtpd_draft_tail(const uint16_t* hidden, const uint16_t* residual, const float* norm_weight, float eps,
+                            int64_t M, int64_t H, const mtpd_fp8_weight* w, uint16_t* out_hidden,
+                            const mtpd_qact* out_act, float* out_max, int32_t* out_idx, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    mtpd_status st = check_norm_args(hidden, residual, norm_weight, M, H, out_hidden, out_act);
+    if (st != MTPD_OK) return st;
+    st = check_weight(w, H);
+    if (st != MTPD_OK) return st;
+    if (M == 0) return MTPD_OK;
+    st = check_lmhead_outputs(M, out_max, out_idx, workspace, workspace_bytes);
+    if (st != MTPD_OK) return st;
+    const size_t mh = (size_t)M * (size_t)H;
+    const Range outs[] = {{out_hidden, mh * 2, "out_hidden"},
+                          {out_act->codes, mh, "out_act.codes"},
+                          {out_act->scales, mh / 128 * 4, "out_act.scales"},
+                          {out_max, (size_t)M * 4, "out_max"},
+                          {out_idx, (size_t)M * 4, "out_idx"},
+                          {workspace, mtpd::workspace_bytes(M), "workspace"}};
+    const Range ins[] = {{hidden, mh * 2, "hidden"},
+                         {residual, mh * 2, "residual"},
+                         {norm_weight, (size_t)H * 4, "norm_weight"},
+                         {w->codes, (size_t)w->V * (size_t)H, "w.codes"},
+                         {w->scales, (size_t)(w->V / 128) * (size_t)(H / 128) * 4, "w.scales"}};
+    st = check_alias(outs, 6, ins, 5);
+    if (st != MTPD_OK) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    st = hip_status(mtpd::launch_norm_quant(hidden, residual, norm_weight, eps, M, H, out_hidden, out_act->codes,
+                                            out_act->scales, s),
+                    "norm_quant launch");
+    if (st != MTPD_OK) return st;
+    mtpd::LmheadArgs a{out_act->codes, out_act->scales, nullptr, M, w->codes, w->scales, w->V, H,
+                       out_max, out_idx, workspace};
+    return hip_status(mtpd::launch_lmhead_argmax(a, s), "lmhead_argmax launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and rejects invalid arguments with typed statuses before any HIP
+call (so nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mtp_draft_head_amd as m
+from mtp_draft_head_amd import FP8Weight, QAct
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mtpd.h")
+
+OK, NULL, SHAPE, ALIGN, ALIAS, WORKSPACE, HIP = range(7)
+A = 0x10000000          # fake, never dereferenced device addresses (validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mtpd_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(m.library_path()):
+        from mtp_draft_head_amd import build
+        build.build()
+    return m.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"mtpd_norm_quant", "mtpd_fp8_lmhead_argmax", "mtpd_draft_tail", "mtpd_workspace_bytes",
+            "mtpd_status_name", "mtpd_last_error", "mtpd_clear_error", "mtpd_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_names_and_version(L):
+    assert [L.mtpd_status_name(i).decode() for i in range(7)] == [
+        "MTPD_OK", "MTPD_ERR_NULL", "MTPD_ERR_SHAPE", "MTPD_ERR_ALIGN", "MTPD_ERR_ALIAS",
+        "MTPD_ERR_WORKSPACE", "MTPD_ERR_HIP"]
+    assert L.mtpd_status_name(99).decode() == "MTPD_UNKNOWN"
+    assert L.mtpd_abi_version() == 1
+
+
+def test_workspace_bytes(L):
+    assert L.mtpd_workspace_bytes(0) == 0
+    assert L.mtpd_workspace_bytes(-3) == 0
+    assert L.mtpd_workspace_bytes(1) == 256
+    assert L.mtpd_workspace_bytes(31) == 256
+    assert L.mtpd_workspace_bytes(32) == 512
+    assert L.mtpd_workspace_bytes(8192) == 65792
+    for n in (1, 7, 64, 320, 8192):
+        assert L.mtpd_workspace_bytes(n) >= 8 * n + 4
+        assert L.mtpd_workspace_bytes(n) % 256 == 0
+
+
+def nq(L, hidden=A, residual=A + 0x1000000, g=A + 0x2000000, M=4, H=256, out_h=A + 0x3000000,
+       codes=A + 0x4000000, scales=A + 0x5000000, rows=None, cols=None):
+    qa = QAct(codes, scales, M if rows is None else rows, H if cols is None else cols)
+    L.mtpd_clear_error()
+    return L.mtpd_norm_quant(hidden, residual, g, 1e-6, M, H, out_h, ctypes.byref(qa), None)
+
+
+def test_norm_quant_validation(L):
+    assert nq(L, hidden=None) == NULL
+    assert "NULL" in L.mtpd_last_error().decode()
+    assert nq(L, H=200) == SHAPE
+    assert nq(L, H=0) == SHAPE
+    assert nq(L, H=16384 + 128, cols=16384 + 128) == SHAPE
+    assert nq(L, M=-1) == SHAPE
+    assert nq(L, rows=3) == SHAPE
+    assert nq(L, cols=128) == SHAPE
+    assert nq(L, hidden=A + 8) == ALIGN
+    assert nq(L, codes=A + 0x4000000 + 4) == ALIGN
+    assert nq(L, scales=A + 0x5000000 + 2) == ALIGN
+    assert nq(L, out_h=A) == ALIAS                       # output over the hidden input
+    assert nq(L, codes=A + 0x3000000 + 512) == ALIAS     # codes inside out_hidden
+    assert nq(L, M=0) == OK                              # empty call: nothing to do, nothing launched
+    assert L.mtpd_norm_quant(A, A, A, 1e-6, 4, 256, A, None, None) == NULL
+
+
+def test_first_error_is_kept_until_cleared(L):
+    L.mtpd_clear_error()
+    qa = QAct(A + 0x4000000, A + 0x5000000, 4, 256)
+    assert L.mtpd_norm_quant(None, A, A, 1e-6, 4, 256, A, ctypes.byref(qa), None) == NULL
+    first = L.mtpd_last_error().decode()
+    assert L.mtpd_norm_quant(A, A, A, 1e-6, 4, 200, A, ctypes.byref(qa), None) == SHAPE
+    assert L.mtpd_last_error().decode() == first
+    L.mtpd_clear_error()
+    assert L.mtpd_last_error().decode() == ""
+
+
+def lm(L, M=4, H=256, V=1024, act_rows=None, act_codes=A, act_scales=A + 0x100000, row_index=None,
+       w_codes=A + 0x1000000, w_scales=A + 0x2000000, wV=None, wH=None, out_max=A + 0x3000000,
+       out_idx=A + 0x3100000, ws=A + 0x4000000, ws_bytes=None):
+    qa = QAct(act_codes, act_scales, M if act_rows is None else act_rows, H)
+    w = FP8Weight(w_codes, w_scales, V if wV is None else wV, H if wH is None else wH)
+    if ws_bytes is None:
+        ws_bytes = L.mtpd_workspace_bytes(M)
+    L.mtpd_clear_error()
+    return L.mtpd_fp8_lmhead_argmax(ctypes.byref(qa), row_index, M, ctypes.byref(w), out_max, out_idx,
+                                    ws, ws_bytes, None)
+
+
+def test_lmhead_validation(L):
+    assert lm(L, act_codes=None) == NULL
+    assert lm(L, w_codes=None) == NULL
+    assert lm(L, out_idx=None) == NULL
+    assert lm(L, V=1000) == SHAPE
+    assert lm(L, V=1 << 31, wV=1 << 31) == SHAPE
+    assert lm(L, wH=512) == SHAPE
+    assert lm(L, M=5, act_rows=4) == SHAPE               # more rows than the activation, no row_index
+    assert lm(L, M=-2) == SHAPE
+    assert lm(L, w_codes=A + 0x1000000 + 1) == ALIGN
+    assert lm(L, ws=A + 0x4000000 + 64) == ALIGN
+    assert lm(L, ws=None) == WORKSPACE
+    assert lm(L, ws_bytes=16) == WORKSPACE
+    assert lm(L, out_max=A + 0x1000000 + 64) == ALIAS     # output inside the weight codes
+    assert lm(L, out_idx=A + 0x3000000) == ALIAS          # two outputs overlap
+    assert lm(L, ws=A + 0x100000) == ALIAS                # workspace over the activation scales
+    assert lm(L, M=0) == OK
+
+
+def test_draft_tail_validation(L):
+    def dt(M=4, H=256, V=1024, wH=None, ws_bytes=None, out_max=A + 0x6000000, hidden=A):
+        qa = QAct(A + 0x4000000, A + 0x5000000, M, H)
+        w = FP8Weight(A + 0x7000000, A + 0x8000000, V, H if wH is None else wH)
+        L.mtpd_clear_error()
+        return L.mtpd_draft_tail(hidden, A + 0x1000000, A + 0x2000000, 1e-6, M, H, ctypes.byref(w),
+                                 A + 0x3000000, ctypes.byref(qa), out_max, A + 0x6100000, A + 0x9000000,
+                                 L.mtpd_workspace_bytes(M) if ws_bytes is None else ws_bytes, None)
+    assert dt(hidden=None) == NULL
+    assert dt(wH=512) == SHAPE
+    assert dt(V=100) == SHAPE
+    assert dt(ws_bytes=8) == WORKSPACE
+    assert dt(out_max=A + 0x7000000) == ALIAS
+    assert dt(M=0) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        m.norm_quant(x, x, torch.ones(256), 1e-6)
