@@ -25,16 +25,44 @@ struct LmheadArgs {
     int64_t H;
     float* out_max;
     int32_t* out_idx;
-    void* workspace;            // [n_rows] u64 keys, then a u32 completion counter
+    void* workspace;            // layout below
 };
 
 hipError_t launch_lmhead_argmax(const LmheadArgs& a, hipStream_t stream);
 
-// Workspace layout shared by the launcher and the C ABI.
+// the decode-regime kernel (lmhead_decode.hip): n_rows <= 64
+bool decode_config_compiled(int mt, int nt, int d);
+size_t decode_config_lds(int mt, int d, int KB);
+hipError_t launch_lmhead_decode(const LmheadArgs& a, int mt, int nt, int d, hipStream_t stream);
+
+// Workspace of the LM-head kernels (all of it zero between calls):
+//   keys      P partitions x n_rows u64 argmax keys.  While P * n_rows <= 4096
+//             every key sits on its own 128-byte line (stride 16 u64), so
+//             workgroups merging into different slots never share a line;
+//             beyond that (large n_rows, P = 1) keys are dense.
+//   counters  33 u32 arrival counters, one per 128-byte line (32 groups +
+//             the top), after the keys padded to 256 bytes.
+constexpr int kArriveGroups = 32;
+
+inline int workspace_partitions(int64_t n_rows) {
+    int P = 256;
+    while (P > 1 && (int64_t)P * n_rows > 4096) P >>= 1;
+    return P;
+}
+
+inline int workspace_key_stride(int64_t n_rows) {
+    return (int64_t)workspace_partitions(n_rows) * n_rows <= 4096 ? 16 : 1;
+}
+
+inline size_t workspace_key_bytes(int64_t n_rows) {
+    const size_t raw =
+        (size_t)workspace_partitions(n_rows) * (size_t)n_rows * (size_t)workspace_key_stride(n_rows) * 8;
+    return (raw + 255) & ~(size_t)255;
+}
+
 inline size_t workspace_bytes(int64_t n_rows) {
     if (n_rows <= 0) return 0;
-    const size_t raw = (size_t)n_rows * 8 + 8;
-    return (raw + 255) & ~(size_t)255;
+    return workspace_key_bytes(n_rows) + (size_t)(kArriveGroups + 1) * 128 + 128;   // padded to 256
 }
 
 }  // namespace mtpd

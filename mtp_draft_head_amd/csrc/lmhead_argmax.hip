@@ -37,41 +37,58 @@
 // In the weight-streaming (decode) regime the cost is the weight read:
 // V*H code bytes + V*H/16384*4 scale bytes per call.
 
+#include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
-#include "device_common.h"
 #include "kernels.h"
+#include "lmhead_common.h"
 
 namespace mtpd {
 
-__device__ __forceinline__ v8i load_frag(const uint8_t* p) {
-    const uint4 lo = *reinterpret_cast<const uint4*>(p);
-    const uint4 hi = *reinterpret_cast<const uint4*>(p + 64);
-    v8i f;
-    f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
-    f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
-    return f;
+// f_lds[kb * ROWS + r] = sa[row r of the tile][kb] * sw[kb] for the tile's
+// ROWS rows.  Loads are issued in batches with clamped (never branching)
+// indices so each batch costs one memory latency; out-of-range slots are
+// simply not stored.
+template <bool GATHER, int ROWS, int NTHREADS>
+__device__ __forceinline__ void stage_scales(float* f_lds, const float* __restrict__ a_scales,
+                                             const int32_t* __restrict__ row_index,
+                                             const float* __restrict__ swp, int m0, int n_rows, int KB) {
+    const int n = KB * ROWS;
+    constexpr int BATCH = 16;
+    for (int base = 0; base < n; base += NTHREADS * BATCH) {
+        float v[BATCH];
+        int dst[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+            const int e = base + i * NTHREADS + (int)threadIdx.x;
+            const int ec = min(e, n - 1);
+            const int r = ec / KB, kb = ec - r * KB;
+            const int m = min(m0 + r, n_rows - 1);
+            const int a = GATHER ? row_index[m] : m;
+            v[i] = a_scales[(size_t)a * KB + kb] * swp[kb];
+            dst[i] = e < n ? kb * ROWS + r : -1;
+        }
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i)
+            if (dst[i] >= 0) f_lds[dst[i]] = v[i];
+    }
 }
 
-__device__ __forceinline__ v4f mfma_e4m3(v8i a, v8i b) {
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    // format selectors 0/0 = E4M3 for both operands; zero block scales select
-    // the unscaled instruction.
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
-}
-
-template <int MT, int NT, int S>
+template <int MT, int NT, int S, int D>
 __global__ __launch_bounds__(64 * S) void lmhead_argmax_kernel(
     const uint8_t* __restrict__ a_codes, const float* __restrict__ a_scales,
     const int32_t* __restrict__ row_index, int n_rows,
     const uint8_t* __restrict__ w_codes, const float* __restrict__ w_scales, int H,
     int n_row_tiles, int total_tiles,
     float* __restrict__ out_max, int32_t* __restrict__ out_idx,
-    unsigned long long* __restrict__ keys, unsigned int* __restrict__ counter)
+    ArgmaxWs ws)
 {
     constexpr int ROWS = MT * 16;
     constexpr int COLS = NT * 16;
     extern __shared__ float lds[];
+    __shared__ unsigned long long red[64 * S];
+    __shared__ int last_flag;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -81,15 +98,6 @@ __global__ __launch_bounds__(64 * S) void lmhead_argmax_kernel(
     const int m0 = rt * ROWS;
     const int n0 = (tile / n_row_tiles) * COLS;
     const int vb = n0 >> 7;
-
-    // activation scales of this row tile, K-major: sa_lds[kb * ROWS + r]
-    float* sa_lds = lds;
-    for (int e = threadIdx.x; e < KB * ROWS; e += 64 * S) {
-        const int r = e / KB, kb = e - r * KB;
-        const int m = min(m0 + r, n_rows - 1);
-        const int a = row_index ? row_index[m] : m;
-        sa_lds[kb * ROWS + r] = a_scales[(size_t)a * KB + kb];
-    }
 
     const uint8_t* ap[MT];
 #pragma unroll
@@ -102,10 +110,15 @@ __global__ __launch_bounds__(64 * S) void lmhead_argmax_kernel(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
         wp[nt] = w_codes + (size_t)(n0 + nt * 16 + (lane & 15)) * H + (lane >> 4) * 16;
-    const float* swp = w_scales + (size_t)vb * KB;
 
-    __syncthreads();
+    const int kb0 = (wave * KB) / S;
+    const int kb1 = ((wave + 1) * KB) / S;
 
+    // D-deep register ring: block kb+D is requested as soon as block kb has
+    // been consumed, so D K blocks per wave are always in flight, and the
+    // D blocks of one refill are consecutive 128-byte pieces of each row.
+    // Only fragment loads sit in the vector-memory queue inside the loop (the
+    // scales come from LDS), so each wait is for the oldest block alone.
     float acc[MT][NT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -114,43 +127,75 @@ __global__ __launch_bounds__(64 * S) void lmhead_argmax_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[mt][nt][i] = 0.f;
 
-    const int kb0 = (wave * KB) / S;
-    const int kb1 = ((wave + 1) * KB) / S;
-
-    auto load = [&](v8i (&af)[MT], v8i (&wf)[NT], int kb) {
+    v8i af[D][MT], wf[D][NT];
+    float* f_lds = lds;   // [KB][ROWS]: sa[row][kb] * sw[vb][kb]
+    auto load = [&](int j, int kb) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) wf[nt] = load_frag(wp[nt] + kb * kBlock);
+        for (int nt = 0; nt < NT; ++nt) wf[j][nt] = load_frag(wp[nt] + kb * kBlock);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) af[mt] = load_frag(ap[mt] + kb * kBlock);
+        for (int mt = 0; mt < MT; ++mt) af[j][mt] = load_frag(ap[mt] + kb * kBlock);
     };
-    auto compute = [&](const v8i (&af)[MT], const v8i (&wf)[NT], int kb) {
-        const float sw = swp[kb];
+    auto compute = [&](int j, int kb) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const float4 sa = *reinterpret_cast<const float4*>(&sa_lds[kb * ROWS + mt * 16 + 4 * (lane >> 4)]);
-            const float f[4] = {sa.x * sw, sa.y * sw, sa.z * sw, sa.w * sw};
+            const float4 f = *reinterpret_cast<const float4*>(&f_lds[kb * ROWS + mt * 16 + 4 * (lane >> 4)]);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const v4f p = mfma_e4m3(af[mt], wf[nt]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(p[i], f[i], acc[mt][nt][i]);
+                const v4f p = mfma_e4m3(af[j][mt], wf[j][nt]);
+                acc[mt][nt][0] = fmaf(p[0], f.x, acc[mt][nt][0]);
+                acc[mt][nt][1] = fmaf(p[1], f.y, acc[mt][nt][1]);
+                acc[mt][nt][2] = fmaf(p[2], f.z, acc[mt][nt][2]);
+                acc[mt][nt][3] = fmaf(p[3], f.w, acc[mt][nt][3]);
             }
         }
     };
 
-    v8i a0[MT], w0[NT], a1[MT], w1[NT];
-    int kb = kb0;
-    if (kb < kb1) load(a0, w0, kb);
-    for (; kb + 1 < kb1; kb += 2) {
-        load(a1, w1, kb + 1);
-        compute(a0, w0, kb);
-        if (kb + 2 < kb1) load(a0, w0, kb + 2);
-        compute(a1, w1, kb + 1);
+    // Prologue: first the ring's first D blocks, then the combined scale
+    // table of this row tile (sa * sw, K-major), whose loads overlap theirs.
+    const bool ring = kb1 - kb0 >= D;
+    if (ring) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) load(j, kb0 + j);
     }
-    if (kb < kb1) compute(a0, w0, kb);
+    {
+        const float* swp = w_scales + (size_t)vb * KB;
+        if (row_index)
+            stage_scales<true, ROWS, 64 * S>(f_lds, a_scales, row_index, swp, m0, n_rows, KB);
+        else
+            stage_scales<false, ROWS, 64 * S>(f_lds, a_scales, row_index, swp, m0, n_rows, KB);
+    }
+    __syncthreads();
+
+    int kb = kb0;
+    if (ring) {
+        for (; kb + 2 * D <= kb1; kb += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                compute(j, kb + j);
+                load(j, kb + D + j);
+                // keep the consume/refill order: without this the scheduler
+                // hoists all D MFMAs above the refills and waits for the whole
+                // ring at once
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < D; ++j) compute(j, kb + j);
+        kb += D;
+    }
+    // fewer than D blocks left: request them all (indices clamped, so the
+    // requests are unconditional), then consume the valid ones
+    const int rem = kb1 - kb;
+    if (rem > 0) {
+#pragma unroll
+        for (int j = 0; j < D - 1; ++j) load(j, min(kb + j, kb1 - 1));
+#pragma unroll
+        for (int j = 0; j < D - 1; ++j)
+            if (j < rem) compute(j, kb + j);
+    }
 
     if constexpr (S > 1) {
-        float* part = lds + KB * ROWS;   // [(S-1)][MT*NT*4][64]
+        float* part = lds + KB * ROWS;   // [(S-1)][MT*NT*4][64], after the scale table
         constexpr int NE = MT * NT * 4;
         if (wave > 0) {
 #pragma unroll
@@ -162,57 +207,69 @@ __global__ __launch_bounds__(64 * S) void lmhead_argmax_kernel(
                         part[((wave - 1) * NE + (mt * NT + nt) * 4 + i) * 64 + lane] = acc[mt][nt][i];
         }
         __syncthreads();
-        if (wave > 0) return;
+        if (wave == 0) {
 #pragma unroll
-        for (int w = 1; w < S; ++w)
+            for (int w = 1; w < S; ++w)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
+                    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[mt][nt][i] += part[((w - 1) * NE + (mt * NT + nt) * 4 + i) * 64 + lane];
-    }
-
-    // wave 0: per-row best key of this tile, merged across workgroups
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint64_t best = 0;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                best = u64_max(best, argmax_key(acc[mt][nt][i], (uint32_t)(n0 + nt * 16 + (lane & 15))));
-#pragma unroll
-            for (int off = 8; off > 0; off >>= 1) best = u64_max(best, shfl_xor_u64(best, off));
-            const int row = m0 + mt * 16 + 4 * (lane >> 4) + i;
-            if ((lane & 15) == 0 && row < n_rows)
-                atomicMax(&keys[row], (unsigned long long)best);
+                        for (int i = 0; i < 4; ++i)
+                            acc[mt][nt][i] += part[((w - 1) * NE + (mt * NT + nt) * 4 + i) * 64 + lane];
         }
     }
 
-    __threadfence();
-    unsigned int prev = 0;
-    if (lane == 0) prev = atomicAdd(counter, 1u);
-    prev = __shfl(prev, 0);
-    if (prev != (unsigned int)(total_tiles - 1)) return;
-
-    // last workgroup: every other workgroup's keys are visible
-    __threadfence();
-    for (int r = lane; r < n_rows; r += 64) {
-        const uint64_t k = __hip_atomic_load(&keys[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        out_max[r] = key_value(k);
-        out_idx[r] = key_index(k);
-        __hip_atomic_store(&keys[r], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // wave 0: per-row best key of this tile (16-lane shuffle reduction over
+    // the tile's columns), then one merge per row and the arrival.
+    if (wave == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint64_t best = 0;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    best = u64_max(best, argmax_key(acc[mt][nt][i], (uint32_t)(n0 + nt * 16 + (lane & 15))));
+#pragma unroll
+                for (int off = 8; off > 0; off >>= 1) best = u64_max(best, shfl_xor_u64(best, off));
+                if ((lane & 15) == 0) red[mt * 16 + 4 * (lane >> 4) + i] = best;
+            }
+        }
+        // ROWS <= 64: lane r merges row m0 + r
+        uint64_t old = 0;
+        if (lane < ROWS && m0 + lane < n_rows) old = merge_key(ws, n_rows, tile, m0 + lane, red[lane]);
+        const unsigned int dep = __builtin_amdgcn_ballot_w64(never_nonzero(old) != 0) != 0 ? 1u : 0u;
+        bool last = false;
+        if (lane == 0) last = arrive(ws, tile, total_tiles, dep);
+        if (lane == 0) last_flag = last ? 1 : 0;
     }
-    if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (!last_flag) return;
+    finalize_argmax<64 * S>(ws, n_rows, out_max, out_idx, red);
 }
 
 namespace {
 
 struct Tile {
-    int mt, nt, s;
+    int mt, nt, s, d;
 };
+
+// (MT row tiles, NT column tiles per wave, S split-K waves, D ring depth)
+// combinations compiled into the library.
+#define MTPD_LM_CONFIGS(X)                                                                       \
+    X(1, 1, 1, 8) X(1, 1, 2, 8) X(1, 1, 3, 8) X(1, 1, 4, 8) X(1, 1, 6, 8) X(1, 1, 8, 8)          \
+    X(1, 1, 1, 4) X(1, 1, 2, 4) X(1, 1, 3, 4) X(1, 1, 4, 4) X(1, 1, 6, 4) X(1, 1, 8, 4)          \
+    X(1, 2, 1, 4) X(1, 2, 2, 4) X(1, 2, 3, 4) X(1, 2, 4, 4) X(1, 2, 6, 4) X(1, 2, 8, 4)          \
+    X(2, 2, 1, 4) X(2, 2, 2, 4) X(2, 2, 4, 4) X(2, 4, 1, 2) X(2, 4, 2, 2) X(2, 4, 4, 2)          \
+    X(4, 2, 1, 2) X(4, 2, 2, 2) X(4, 2, 4, 2) X(4, 4, 1, 2) X(4, 4, 2, 2) X(4, 4, 4, 2)
+
+bool compiled(const Tile& t) {
+#define MTPD_X(a, b, c, e) if (t.mt == a && t.nt == b && t.s == c && t.d == e) return true;
+    MTPD_LM_CONFIGS(MTPD_X)
+#undef MTPD_X
+    return false;
+}
 
 int device_cus() {
     static int cached[64] = {0};
@@ -232,75 +289,101 @@ size_t lds_bytes(const Tile& t, int KB) {
 }
 
 Tile choose_tile(int64_t n_rows, int64_t V, int64_t H) {
+    const int KB = (int)(H / kBlock);
     Tile t;
     t.mt = n_rows <= 16 ? 1 : (n_rows <= 32 ? 2 : 4);
-    t.nt = t.mt == 1 ? 2 : 4;
-    const int KB = (int)(H / kBlock);
-    // optional launch-shape override for tuning sweeps: MTPD_LMHEAD_TILE="nt,s"
-    int env_nt = 0, env_s = 0;
-    if (const char* e = getenv("MTPD_LMHEAD_TILE")) {
-        if (sscanf(e, "%d,%d", &env_nt, &env_s) != 2) env_nt = env_s = 0;
-    }
-    if (env_nt == 1 || env_nt == 2 || env_nt == 4) t.nt = env_nt;
+    t.nt = t.mt == 1 ? 1 : (t.mt == 2 ? 2 : 4);
+    t.d = t.mt == 1 ? 8 : (t.mt == 2 ? 4 : 2);
     const int64_t row_tiles = (n_rows + t.mt * 16 - 1) / (t.mt * 16);
     const int64_t tiles = row_tiles * (V / (t.nt * 16));
     const int64_t want_waves = 8LL * device_cus();
+    // split K across waves only when there are too few tiles to keep every CU
+    // streaming (measured on the 1-row, 18944-row shard: 1184 single-wave
+    // tiles, unsplit, beat any split)
     t.s = 1;
-    while (t.s < 8 && tiles * t.s < want_waves && 2 * t.s <= KB) t.s *= 2;
-    if (env_s == 1 || env_s == 2 || env_s == 4 || env_s == 8) t.s = env_s;
-    // 512-thread workgroups cap a thread at 256 registers: only small tiles fit
-    if (t.s == 8 && t.mt * t.nt > 4) t.s = 4;
-    while (t.s > 1 && lds_bytes(t, KB) > 64 * 1024) t.s /= 2;
+    if (t.mt == 1) t.d = 4;
+    while (t.s < 4 && tiles * t.s < want_waves / 4 && 2 * t.s * t.d <= KB) t.s *= 2;
+    // optional launch-shape override for tuning sweeps: MTPD_LMHEAD_TILE="nt,s,d"
+    if (const char* e = getenv("MTPD_LMHEAD_TILE")) {
+        Tile o = t;
+        if (sscanf(e, "%d,%d,%d", &o.nt, &o.s, &o.d) == 3 && compiled(o)) t = o;
+    }
+    while (!compiled(t) || lds_bytes(t, KB) > 64 * 1024) {
+        if (t.s > 1) t.s /= 2;
+        else if (t.d > 2) t.d /= 2;
+        else break;
+    }
     return t;
 }
 
-template <int MT, int NT, int S>
+template <int MT, int NT, int S, int D>
 hipError_t launch_t(const LmheadArgs& a, hipStream_t stream) {
     const int KB = (int)(a.H / kBlock);
     const int64_t row_tiles = (a.n_rows + MT * 16 - 1) / (MT * 16);
     const int64_t tiles = row_tiles * (a.V / (NT * 16));
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const size_t lds = lds_bytes(Tile{MT, NT, S}, KB);
-    unsigned long long* keys = reinterpret_cast<unsigned long long*>(a.workspace);
-    unsigned int* counter = reinterpret_cast<unsigned int*>(keys + a.n_rows);
-    hipLaunchKernelGGL((lmhead_argmax_kernel<MT, NT, S>), dim3((unsigned)tiles), dim3(64 * S), lds, stream,
+    const size_t lds = lds_bytes(Tile{MT, NT, S, D}, KB);
+    hipLaunchKernelGGL((lmhead_argmax_kernel<MT, NT, S, D>), dim3((unsigned)tiles), dim3(64 * S), lds, stream,
                        a.a_codes, a.a_scales, a.row_index, (int)a.n_rows, a.w_codes, a.w_scales, (int)a.H,
-                       (int)row_tiles, (int)tiles, a.out_max, a.out_idx, keys, counter);
+                       (int)row_tiles, (int)tiles, a.out_max, a.out_idx, argmax_ws(a.workspace, a.n_rows));
     return hipGetLastError();
 }
 
-template <int MT, int NT>
-hipError_t launch_s(const LmheadArgs& a, int s, hipStream_t stream) {
-    switch (s) {
-        case 1: return launch_t<MT, NT, 1>(a, stream);
-        case 2: return launch_t<MT, NT, 2>(a, stream);
-        case 4: return launch_t<MT, NT, 4>(a, stream);
-        case 8:
-            if constexpr (MT * NT <= 4) return launch_t<MT, NT, 8>(a, stream);
-            break;
-    }
-    return hipErrorInvalidValue;
-}
+}  // namespace
 
-template <int MT>
-hipError_t launch_n(const LmheadArgs& a, int nt, int s, hipStream_t stream) {
-    switch (nt) {
-        case 1: return launch_s<MT, 1>(a, s, stream);
-        case 2: return launch_s<MT, 2>(a, s, stream);
-        case 4: return launch_s<MT, 4>(a, s, stream);
+namespace {
+
+struct DecodeTile {
+    int mt, nt, d;
+};
+
+// The decode kernel serves n_rows <= 64 when a compiled (MT, NT, D) fits:
+// D must divide H/128, 64*NT must divide V, and the LDS budget is 64 KB.
+bool choose_decode(int64_t n_rows, int64_t V, int64_t H, DecodeTile* out) {
+    // up to 16 rows the activation is small enough that single-wave tiles of
+    // the generic kernel stream the weight faster than the LDS-sharing workgroups
+    if (n_rows > 64 || n_rows <= 16) return false;
+    const int KB = (int)(H / kBlock);
+    const int mt = n_rows <= 16 ? 1 : (n_rows <= 32 ? 2 : 4);
+    DecodeTile cand[6];
+    int nc = 0;
+    if (const char* e = getenv("MTPD_LMHEAD_DECODE")) {   // tuning override "nt,d"
+        DecodeTile o{mt, 0, 0};
+        if (sscanf(e, "%d,%d", &o.nt, &o.d) == 2) cand[nc++] = o;
     }
-    return hipErrorInvalidValue;
+    if (mt == 1) {
+        cand[nc++] = {1, 1, 8};
+        cand[nc++] = {1, 1, 4};
+    } else if (mt == 2) {
+        cand[nc++] = {2, 1, 4};
+        cand[nc++] = {2, 2, 4};
+    } else {
+        cand[nc++] = {4, 2, 2};
+        cand[nc++] = {4, 1, 4};
+    }
+    for (int i = 0; i < nc; ++i) {
+        const DecodeTile& c = cand[i];
+        if (!decode_config_compiled(c.mt, c.nt, c.d)) continue;
+        if (KB % c.d || V % (64 * c.nt)) continue;
+        if (decode_config_lds(c.mt, c.d, KB) > 64 * 1024) continue;
+        *out = c;
+        return true;
+    }
+    return false;
 }
 
 }  // namespace
 
 hipError_t launch_lmhead_argmax(const LmheadArgs& a, hipStream_t stream) {
+    const char* kind = getenv("MTPD_LMHEAD_KERNEL");   // "generic" forces the tiled kernel (testing)
+    DecodeTile dt;
+    if (!(kind && strcmp(kind, "generic") == 0) && choose_decode(a.n_rows, a.V, a.H, &dt))
+        return launch_lmhead_decode(a, dt.mt, dt.nt, dt.d, stream);
     const Tile t = choose_tile(a.n_rows, a.V, a.H);
-    switch (t.mt) {
-        case 1: return launch_n<1>(a, t.nt, t.s, stream);
-        case 2: return launch_n<2>(a, t.nt, t.s, stream);
-        case 4: return launch_n<4>(a, t.nt, t.s, stream);
-    }
+#define MTPD_X(p, q, r, u) \
+    if (t.mt == p && t.nt == q && t.s == r && t.d == u) return launch_t<p, q, r, u>(a, stream);
+    MTPD_LM_CONFIGS(MTPD_X)
+#undef MTPD_X
     return hipErrorInvalidValue;
 }
 

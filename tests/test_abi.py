@@ -48,15 +48,22 @@ def test_status_names_and_version(L):
 
 
 def test_workspace_bytes(L):
+    # P key partitions (256 halved until P * n_rows <= 4096, at least 1); while
+    # P * n_rows <= 4096 each key has its own 128-byte line, else keys are dense;
+    # padded to 256 bytes, then 33 counters on 128-byte lines (4352 bytes)
+    def expect(n):
+        P = 256
+        while P > 1 and P * n > 4096:
+            P //= 2
+        stride = 16 if P * n <= 4096 else 1
+        return -(-P * n * stride * 8 // 256) * 256 + 4352
     assert L.mtpd_workspace_bytes(0) == 0
     assert L.mtpd_workspace_bytes(-3) == 0
-    assert L.mtpd_workspace_bytes(1) == 256
-    assert L.mtpd_workspace_bytes(31) == 256
-    assert L.mtpd_workspace_bytes(32) == 512
-    assert L.mtpd_workspace_bytes(8192) == 65792
-    for n in (1, 7, 64, 320, 8192):
-        assert L.mtpd_workspace_bytes(n) >= 8 * n + 4
+    for n in (1, 7, 30, 31, 64, 65, 320, 4096, 4097, 8192, 1 << 24):
+        assert L.mtpd_workspace_bytes(n) == expect(n), n
         assert L.mtpd_workspace_bytes(n) % 256 == 0
+    assert L.mtpd_workspace_bytes(1) == 32768 + 4352
+    assert L.mtpd_workspace_bytes(8192) == 65536 + 4352
 
 
 def nq(L, hidden=A, residual=A + 0x1000000, g=A + 0x2000000, M=4, H=256, out_h=A + 0x3000000,
@@ -120,6 +127,7 @@ def test_lmhead_validation(L):
     assert lm(L, ws=A + 0x4000000 + 64) == ALIGN
     assert lm(L, ws=None) == WORKSPACE
     assert lm(L, ws_bytes=16) == WORKSPACE
+    assert lm(L, ws_bytes=L.mtpd_workspace_bytes(4) - 256) == WORKSPACE
     assert lm(L, out_max=A + 0x1000000 + 64) == ALIAS     # output inside the weight codes
     assert lm(L, out_idx=A + 0x3000000) == ALIAS          # two outputs overlap
     assert lm(L, ws=A + 0x100000) == ALIAS                # workspace over the activation scales

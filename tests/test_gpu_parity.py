@@ -88,7 +88,7 @@ def check_lmhead(codes, scales, d, gmax, gidx, rows=None):
 
 SHAPES = [
     (1, 128, 128), (4, 256, 1024), (5, 384, 640), (17, 640, 1152), (33, 1024, 384),
-    (64, 2048, 2048), (65, 768, 256), (130, 256, 512), (3, 16384, 256), (2, 6144, 18944 // 8),
+    (64, 2048, 2048), (65, 768, 256), (130, 256, 512), (3, 16384, 256), (2, 6144, 2304),
 ]
 
 
@@ -237,7 +237,9 @@ def test_workload_full_size(name, workloads):
 def test_vocab_shards_combine_to_full_vocab(workloads):
     """The decode c=64 weight cut into 8 vocab shards of 18944 rows: each shard's
     local (max, idx) pairs, combined by largest max then lowest global index,
-    equal the full-vocab result."""
+    give the full-vocab argmax (checked against the oracle, and index for index
+    against the single full-vocab launch outside near-ties; shard and full
+    launches may split K differently, so max values agree to rounding)."""
     d = workloads("decode_c64_full")
     h, r, g, wc, ws = to_dev(d)
     _, codes, scales, gmax, gidx = mtpd.draft_tail(h, r, g, d["eps"], wc, ws)
@@ -248,5 +250,12 @@ def test_vocab_shards_combine_to_full_vocab(workloads):
         maxes.append(host(m))
         idxs.append(host(i))
     cm, ci = oracle.combine_shards(np.stack(maxes), np.stack(idxs), [k * S for k in range(8)])
-    assert np.array_equal(ci, host(gidx).astype(np.int64))
-    assert np.array_equal(cm, host(gmax))
+    c, s = host(codes), host(scales)
+    ref = oracle.argmax(c, s, d["w_codes"], d["w_scales"])
+    rep = parity.check_argmax(cm, ci, ref,
+                              logit_row=lambda i: oracle.logits(c, s, d["w_codes"], d["w_scales"], rows=[i])[0])
+    say(f"  shards vs oracle {rep}")
+    gap = (ref["z1"] - ref["z2"]) / np.abs(ref["z1"])
+    clear = gap > 1e-5
+    assert np.array_equal(ci[clear], host(gidx).astype(np.int64)[clear])
+    assert np.allclose(cm, host(gmax), rtol=1e-5, atol=0)
