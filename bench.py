@@ -32,7 +32,8 @@ METRIC = "draft rows/s + LM-head HBM GB/s (% of peak) for fused norm-quant-FP8-G
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 MFMA
 CACHE_DEFEAT_BYTES = 768 << 20  # rotate weight copies past the 256 MB Infinity Cache
-KERNEL_SOURCES = ["mtp_draft_head_amd/csrc/lmhead_argmax.hip", "mtp_draft_head_amd/csrc/device_common.h",
+KERNEL_SOURCES = ["mtp_draft_head_amd/csrc/lmhead_argmax.hip", "mtp_draft_head_amd/csrc/lmhead_decode.hip",
+                  "mtp_draft_head_amd/csrc/lmhead_common.h", "mtp_draft_head_amd/csrc/device_common.h",
                   "mtp_draft_head_amd/csrc/kernels.h"]
 
 
@@ -65,6 +66,62 @@ def traffic_from_profile(workload: str):
     if t.get("kernel_hash") != kernel_hash():
         return None
     return t.get("bytes_per_launch")
+
+
+def _read_counters(path):
+    """rocprofv3 counter-collection CSV -> list of (kernel_name, counter, value) per dispatch."""
+    import csv
+
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append((r.get("Kernel_Name", ""), r.get("Counter_Name", ""), float(r.get("Counter_Value", 0) or 0),
+                         r.get("Dispatch_Id", "")))
+    return rows
+
+
+def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, copy_mib: int) -> int:
+    """HBM bytes per LM-head launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by the reading of the same counter for the
+    calibration copy, which reads and writes exactly copy_mib MiB.  Writes
+    profiles/lmhead_argmax_<workload>_traffic.json (and prints it)."""
+    from mtp_draft_head_amd import inputs
+
+    if copy_mib <= 0:
+        print("--copy-calibration-mib must give the calibration copy size", file=sys.stderr)
+        return 1
+    w = inputs.get(workload)
+    alg = lmhead_bytes(w.M, w.H, w.V)
+    out = {"workload": workload, "kernel_hash": kernel_hash(), "algorithmic_bytes_per_launch": alg,
+           "calibration_copy_bytes": copy_mib << 20}
+    total = 0.0
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _read_counters(path) if r[1] == counter]
+        copy = [v for k, c, v, _ in rows if "copy" in k.lower()]
+        lm = [v for k, c, v, _ in rows if "lmhead" in k]
+        if not copy or not lm:
+            print(f"no copy or lmhead dispatches with {counter} in {path}", file=sys.stderr)
+            return 1
+        copy_kib = max(copy)                       # the calibration copy is the largest copy
+        factor = (copy_mib << 20) / (copy_kib * 1024.0)
+        lm_bytes = sum(lm) / len(lm) * 1024.0 * factor
+        total += lm_bytes
+        out[counter] = {"lmhead_kib_per_dispatch": sum(lm) / len(lm), "lmhead_dispatches": len(lm),
+                        "copy_kib": copy_kib, "scale": factor, "bytes_per_launch": lm_bytes}
+    out["bytes_per_launch"] = total
+    out["traffic_over_algorithmic"] = total / alg
+    run = f"python3 bench.py --no-cpu-baseline --workload {workload} --steps 20 --warmup 5 --copy-calibration-mib {copy_mib}"
+    out["commands"] = [
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcf_{workload} -o run -- {run}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcw_{workload} -o run -- {run}",
+        f"python3 bench.py --workload {workload} --copy-calibration-mib {copy_mib} --summarize-pmc "
+        f"gpurun_out/pmcf_{workload}/run_counter_collection.csv gpurun_out/pmcw_{workload}/run_counter_collection.csv",
+    ]
+    dst = os.path.join(ROOT, "profiles", f"lmhead_argmax_{workload}_traffic.json")
+    with open(dst, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
 
 
 def cpu_baseline(d, seconds: float):
@@ -101,7 +158,14 @@ def main() -> int:
     ap.add_argument("--workload", default="decode_c1_tp8_shard")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first (a counter reference for PMC runs)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a run with "
+                         "--copy-calibration-mib into the LM-head traffic summary under profiles/")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        return summarize_pmc(args.workload, *args.summarize_pmc, args.copy_calibration_mib)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py drives exactly one GPU: the multi-GPU path (vocab shards combined by a u64 max "
@@ -146,6 +210,18 @@ def main() -> int:
     def lm_step(i):
         mtpd.fp8_lmhead_argmax(out[1], out[2], wcs[i % n_copies], wss[i % n_copies], workspace=wsp, out=lm_out)
 
+    if args.copy_calibration_mib:
+        nb = args.copy_calibration_mib << 20
+        src = torch.ones(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {nb} bytes done")
+        del src, dst
+
+    plan = mtpd.lmhead_plan(M, V, H)
+    log(f"[bench] LM-head plan: {plan}")
     log(f"[bench] warmup {W} eager steps ({n_copies} weight copies, {n_copies * wbytes / 2**20:.0f} MiB)")
     for i in range(W):
         step(i)
@@ -206,7 +282,7 @@ def main() -> int:
     else:
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
-    roof.update({"kernel": "lmhead_argmax_kernel", "avg_launch_us": round(lm_us, 3),
+    roof.update({"kernel": plan, "avg_launch_us": round(lm_us, 3),
                  "algorithmic_bytes_per_launch": alg, "flops_per_launch": flops})
 
     cpu = None

@@ -156,6 +156,12 @@ const char *mtpd_status_name(mtpd_status s);
 const char *mtpd_last_error(void);
 void mtpd_clear_error(void);
 
+/* Diagnostics: the kernel (and launch shape) mtpd_fp8_lmhead_argmax would
+ * run for these sizes, e.g. "lmhead_decode_kernel<4,2,2> grid=1184x256",
+ * as a static thread-local string; "" if the sizes are invalid.  Makes no
+ * HIP call except a one-time query of the current device's CU count. */
+const char *mtpd_lmhead_plan(int64_t n_rows, int64_t V, int64_t H);
+
 /* ABI version: bumped when any declaration above changes. */
 int mtpd_abi_version(void);
 

@@ -29,7 +29,7 @@ import torch
 
 __all__ = [
     "MtpdError", "MtpdLibraryMissing", "norm_quant", "fp8_lmhead_argmax", "draft_tail",
-    "workspace_bytes", "Workspace", "library_path", "lib",
+    "workspace_bytes", "Workspace", "library_path", "lib", "lmhead_plan",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -96,6 +96,8 @@ def lib():
         L.mtpd_last_error.argtypes = []
         L.mtpd_clear_error.restype = None
         L.mtpd_clear_error.argtypes = []
+        L.mtpd_lmhead_plan.restype = ctypes.c_char_p
+        L.mtpd_lmhead_plan.argtypes = [I64, I64, I64]
         L.mtpd_abi_version.restype = ctypes.c_int
         L.mtpd_abi_version.argtypes = []
         _lib = L
@@ -109,6 +111,11 @@ def _check(status: int):
         detail = L.mtpd_last_error().decode()
         L.mtpd_clear_error()
         raise MtpdError(status, name, detail)
+
+
+def lmhead_plan(n_rows: int, V: int, H: int) -> str:
+    """The LM-head kernel and launch shape the library picks for these sizes."""
+    return lib().mtpd_lmhead_plan(int(n_rows), int(V), int(H)).decode()
 
 
 def workspace_bytes(n_rows: int) -> int:

@@ -30,6 +30,9 @@ struct LmheadArgs {
 
 hipError_t launch_lmhead_argmax(const LmheadArgs& a, hipStream_t stream);
 
+// name and launch shape of the kernel launch_lmhead_argmax picks
+void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len);
+
 // the decode-regime kernel (lmhead_decode.hip): n_rows <= 64
 bool decode_config_compiled(int mt, int nt, int d);
 size_t decode_config_lds(int mt, int d, int KB);

@@ -374,10 +374,26 @@ bool choose_decode(int64_t n_rows, int64_t V, int64_t H, DecodeTile* out) {
 
 }  // namespace
 
-hipError_t launch_lmhead_argmax(const LmheadArgs& a, hipStream_t stream) {
+bool use_decode(int64_t n_rows, int64_t V, int64_t H, DecodeTile* dt) {
     const char* kind = getenv("MTPD_LMHEAD_KERNEL");   // "generic" forces the tiled kernel (testing)
+    return !(kind && strcmp(kind, "generic") == 0) && choose_decode(n_rows, V, H, dt);
+}
+
+void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len) {
     DecodeTile dt;
-    if (!(kind && strcmp(kind, "generic") == 0) && choose_decode(a.n_rows, a.V, a.H, &dt))
+    if (use_decode(n_rows, V, H, &dt)) {
+        snprintf(buf, len, "lmhead_decode_kernel<%d,%d,%d> grid=%lldx256", dt.mt, dt.nt, dt.d,
+                 (long long)(V / (64 * dt.nt)));
+        return;
+    }
+    const Tile t = choose_tile(n_rows, V, H);
+    const long long tiles = (long long)((n_rows + t.mt * 16 - 1) / (t.mt * 16)) * (V / (t.nt * 16));
+    snprintf(buf, len, "lmhead_argmax_kernel<%d,%d,%d,%d> grid=%lldx%d", t.mt, t.nt, t.s, t.d, tiles, 64 * t.s);
+}
+
+hipError_t launch_lmhead_argmax(const LmheadArgs& a, hipStream_t stream) {
+    DecodeTile dt;
+    if (use_decode(a.n_rows, a.V, a.H, &dt))
         return launch_lmhead_decode(a, dt.mt, dt.nt, dt.d, stream);
     const Tile t = choose_tile(a.n_rows, a.V, a.H);
 #define MTPD_X(p, q, r, u) \

@@ -134,6 +134,16 @@ void mtpd_clear_error(void) { g_err[0] = 0; }
 
 int mtpd_abi_version(void) { return 1; }
 
+const char* mtpd_lmhead_plan(int64_t n_rows, int64_t V, int64_t H) {
+    thread_local char buf[160];
+    buf[0] = 0;
+    if (n_rows < 1 || n_rows > kMaxRows || H < mtpd::kBlock || H > kMaxH || H % mtpd::kBlock ||
+        V < mtpd::kBlock || V > kMaxV || V % mtpd::kBlock)
+        return buf;
+    mtpd::describe_lmhead(n_rows, V, H, buf, sizeof buf);
+    return buf;
+}
+
 size_t mtpd_workspace_bytes(int64_t n_rows) { return mtpd::workspace_bytes(n_rows); }
 
 mtpd_status mtpd_norm_quant(const uint16_t* hidden, const uint16_t* residual, const float* norm_weight, float eps,

@@ -34,7 +34,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"mtpd_norm_quant", "mtpd_fp8_lmhead_argmax", "mtpd_draft_tail", "mtpd_workspace_bytes",
-            "mtpd_status_name", "mtpd_last_error", "mtpd_clear_error", "mtpd_abi_version"} <= set(names)
+            "mtpd_status_name", "mtpd_last_error", "mtpd_clear_error", "mtpd_abi_version",
+            "mtpd_lmhead_plan"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
