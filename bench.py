@@ -33,6 +33,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 MFMA
 CACHE_DEFEAT_BYTES = 768 << 20  # rotate weight copies past the 256 MB Infinity Cache
 KERNEL_SOURCES = ["mtp_draft_head_amd/csrc/lmhead_argmax.hip", "mtp_draft_head_amd/csrc/lmhead_decode.hip",
+                  "mtp_draft_head_amd/csrc/lmhead_gemm.hip",
                   "mtp_draft_head_amd/csrc/lmhead_common.h", "mtp_draft_head_amd/csrc/device_common.h",
                   "mtp_draft_head_amd/csrc/kernels.h"]
 

@@ -33,6 +33,9 @@ hipError_t launch_lmhead_argmax(const LmheadArgs& a, hipStream_t stream);
 // name and launch shape of the kernel launch_lmhead_argmax picks
 void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len);
 
+// the compute-regime kernel (lmhead_gemm.hip): 256 x 256 tiles, V % 256 == 0
+hipError_t launch_lmhead_gemm(const LmheadArgs& a, hipStream_t stream);
+
 // the decode-regime kernel (lmhead_decode.hip): n_rows <= 64
 bool decode_config_compiled(int mt, int nt, int d);
 size_t decode_config_lds(int mt, int d, int KB);

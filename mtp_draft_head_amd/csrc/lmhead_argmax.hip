@@ -91,7 +91,7 @@ __global__ __launch_bounds__(64 * S) void lmhead_argmax_kernel(
     __shared__ int last_flag;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
     const int KB = H >> 7;
     const int tile = xcd_contiguous((int)blockIdx.x, total_tiles);
     const int rt = tile % n_row_tiles;
@@ -379,8 +379,19 @@ bool use_decode(int64_t n_rows, int64_t V, int64_t H, DecodeTile* dt) {
     return !(kind && strcmp(kind, "generic") == 0) && choose_decode(n_rows, V, H, dt);
 }
 
+// many rows: the LDS-tiled 256 x 256 kernel
+bool use_gemm(int64_t n_rows, int64_t V) {
+    const char* kind = getenv("MTPD_LMHEAD_KERNEL");
+    if (kind && strcmp(kind, "generic") == 0) return false;
+    return n_rows > 64 && V % 256 == 0;
+}
+
 void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len) {
     DecodeTile dt;
+    if (use_gemm(n_rows, V)) {
+        snprintf(buf, len, "lmhead_gemm_kernel grid=%lldx512", (long long)((n_rows + 255) / 256 * (V / 256)));
+        return;
+    }
     if (use_decode(n_rows, V, H, &dt)) {
         snprintf(buf, len, "lmhead_decode_kernel<%d,%d,%d> grid=%lldx256", dt.mt, dt.nt, dt.d,
                  (long long)(V / (64 * dt.nt)));
@@ -392,6 +403,7 @@ void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len
 }
 
 hipError_t launch_lmhead_argmax(const LmheadArgs& a, hipStream_t stream) {
+    if (use_gemm(a.n_rows, a.V)) return launch_lmhead_gemm(a, stream);
     DecodeTile dt;
     if (use_decode(a.n_rows, a.V, a.H, &dt))
         return launch_lmhead_decode(a, dt.mt, dt.nt, dt.d, stream);

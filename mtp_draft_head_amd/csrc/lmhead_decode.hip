@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void lmhead_decode_kernel(
     const int KB = H >> 7;
     const int t = threadIdx.x;
     const int lane = t & 63;
-    const int wave = t >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform, in an SGPR
     const int tile = xcd_contiguous((int)blockIdx.x, total_tiles);
     const int n0 = tile * COLS + wave * WCOLS;      // this wave's first vocab row
 

@@ -195,6 +195,20 @@ def test_every_launch_shape_agrees(tile, monkeypatch):
     assert torch.equal(i0, i1)
 
 
+@pytest.mark.parametrize("kernel", ["generic", "default"])
+def test_many_rows_both_kernels(kernel, monkeypatch):
+    """More than 64 rows: the LDS-tiled 256x256 kernel by default, the generic
+    tiled kernel when forced; both meet the oracle and pick the same indices."""
+    d = inputs.random_case(12, 300, 1024, 1536, outliers=True)
+    h, r, g, wc, ws = to_dev(d)
+    if kernel == "generic":
+        monkeypatch.setenv("MTPD_LMHEAD_KERNEL", "generic")
+    say(f"  plan: {mtpd.lmhead_plan(300, 1536, 1024)}")
+    out_h, codes, scales, gmax, gidx = mtpd.draft_tail(h, r, g, d["eps"], wc, ws)
+    check_norm_quant(d, out_h, codes, scales)
+    check_lmhead(codes, scales, d, gmax, gidx)
+
+
 # --------------------------------------------------------------------------
 # the five workloads at full size
 # --------------------------------------------------------------------------
