@@ -19,6 +19,7 @@ struct LmheadArgs {
     const float* a_scales;
     const int32_t* row_index;   // NULL: identity
     int64_t n_rows;
+    int64_t a_rows;             // rows of the packed activation (row_index values lie below)
     const uint8_t* w_codes;
     const float* w_scales;
     int64_t V;

@@ -380,15 +380,16 @@ bool use_decode(int64_t n_rows, int64_t V, int64_t H, DecodeTile* dt) {
 }
 
 // many rows: the LDS-tiled 256 x 256 kernel
-bool use_gemm(int64_t n_rows, int64_t V) {
+// The tiled kernel addresses the activation with 32-bit byte offsets.
+bool use_gemm(int64_t n_rows, int64_t V, int64_t H, int64_t a_rows) {
     const char* kind = getenv("MTPD_LMHEAD_KERNEL");
     if (kind && strcmp(kind, "generic") == 0) return false;
-    return n_rows > 64 && V % 256 == 0;
+    return n_rows > 64 && V % 256 == 0 && a_rows * H <= ((int64_t)1 << 32);
 }
 
 void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len) {
     DecodeTile dt;
-    if (use_gemm(n_rows, V)) {
+    if (use_gemm(n_rows, V, H, n_rows)) {
         snprintf(buf, len, "lmhead_gemm_kernel grid=%lldx512", (long long)((n_rows + 255) / 256 * (V / 256)));
         return;
     }
@@ -403,7 +404,7 @@ void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len
 }
 
 hipError_t launch_lmhead_argmax(const LmheadArgs& a, hipStream_t stream) {
-    if (use_gemm(a.n_rows, a.V)) return launch_lmhead_gemm(a, stream);
+    if (use_gemm(a.n_rows, a.V, a.H, a.a_rows)) return launch_lmhead_gemm(a, stream);
     DecodeTile dt;
     if (use_decode(a.n_rows, a.V, a.H, &dt))
         return launch_lmhead_decode(a, dt.mt, dt.nt, dt.d, stream);

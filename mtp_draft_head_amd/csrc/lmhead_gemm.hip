@@ -54,6 +54,23 @@ struct Stage {
     float sa[kBM];
 };
 
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their
+// maxima).
+#define MTPD_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+// Position of chunk c (16 bytes, 0..3) of row r's 64-byte K half inside the
+// row's slot of a piece.  The XOR makes the fragment reads conflict-free:
+// the MFMA lanes reading one LDS cycle's worth of 16-byte words (8 or 16
+// consecutive lanes, rows r..r+7 or r..r+15 of one K group) land on distinct
+// bank groups for either LDS bank count.
+__device__ __forceinline__ int piece_chunk(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
+
+// Workgroup barrier without a memory fence: the LDS-DMA copies a wave must
+// have finished are waited for explicitly (MTPD_WAIT_VMCNT) just before, and
+// the memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 __global__ __launch_bounds__(512) void lmhead_gemm_kernel(
     const uint8_t* __restrict__ a_codes, const float* __restrict__ a_scales,
     const int32_t* __restrict__ row_index, int n_rows,
@@ -61,8 +78,8 @@ __global__ __launch_bounds__(512) void lmhead_gemm_kernel(
     int n_row_tiles, int n_col_tiles,
     float* __restrict__ out_max, int32_t* __restrict__ out_idx, ArgmaxWs ws)
 {
-    // two distinct objects, so the compiler can tell an LDS-DMA write into one
-    // from fragment reads of the other and need not drain the DMA before them
+    // two distinct objects, so LDS-DMA writes into one and fragment reads of
+    // the other are independent to the compiler
     __shared__ __align__(16) Stage stage0;
     __shared__ __align__(16) Stage stage1;
     __shared__ unsigned long long red[4 * kBM];
@@ -89,34 +106,47 @@ __global__ __launch_bounds__(512) void lmhead_gemm_kernel(
 
     // staging assignment: wave w copies A pieces and W pieces 4w..4w+3, i.e.
     // 16-row tiles 2w and 2w+1 of each operand, both K halves, straight from
-    // global memory into LDS (no VGPRs); waves 0-3 also copy the 256 scales
-    const uint8_t* ap[2];
-    const uint8_t* wp[2];
+    // global memory into LDS (no VGPRs); waves 0-3 also copy the 256 scales.
+    // In one copy instruction lanes 4q..4q+3 read the four 16-byte chunks of
+    // row q's K half (one 64-byte segment, so the address unit coalesces
+    // them), in the swizzled order piece_chunk(q, .).  Per-lane addresses are
+    // 32-bit byte offsets from wave-uniform bases (the host keeps the
+    // activation under 4 GiB), so a K step only moves the scalar base.
+    const int crow = lane >> 2;
+    const uint32_t cchunk = (uint32_t)piece_chunk(crow, lane & 3) * 16u;
+    uint32_t aoff[2], woff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int m = min(m0 + (2 * wave + i) * 16 + (lane & 15), n_rows - 1);
-        const int a = row_index ? row_index[m] : m;
-        ap[i] = a_codes + (size_t)a * H + (lane >> 4) * 16;
-        wp[i] = w_codes + (size_t)(n0 + (2 * wave + i) * 16 + (lane & 15)) * H + (lane >> 4) * 16;
+        const int m = min(m0 + (2 * wave + i) * 16 + crow, n_rows - 1);
+        const uint32_t a = (uint32_t)(row_index ? row_index[m] : m);
+        aoff[i] = a * (uint32_t)H + cchunk;
+        woff[i] = (uint32_t)((2 * wave + i) * 16 + crow) * (uint32_t)H + cchunk;
     }
+    const uint8_t* wbase = w_codes + (size_t)n0 * (size_t)H;
     const int sa_row = min(m0 + (t & (kBM - 1)), n_rows - 1);
-    const float* sap = a_scales + (size_t)(row_index ? row_index[sa_row] : sa_row) * KB;
+    const uint32_t saoff = (uint32_t)(row_index ? row_index[sa_row] : sa_row) * (uint32_t)KB;
     const float* swp = w_scales + (size_t)((n0 + wn * 64) >> 7) * KB;
 
     auto copy_in = [&](Stage& st, int kb) {
+        const uint8_t* ab = a_codes + (size_t)kb * kBlock;
+        const uint8_t* wb = wbase + (size_t)kb * kBlock;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                __builtin_amdgcn_global_load_lds(ap[i] + kb * kBlock + h * 64,
+                __builtin_amdgcn_global_load_lds(ab + aoff[i] + h * 64,
                                                  (lds_void_ptr)&st.piece[(4 * wave + 2 * i + h) * 64], 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(wp[i] + kb * kBlock + h * 64,
+                __builtin_amdgcn_global_load_lds(wb + woff[i] + h * 64,
                                                  (lds_void_ptr)&st.piece[(kPieces + 4 * wave + 2 * i + h) * 64], 16,
                                                  0, 0);
             }
         }
-        if (wave < 4) __builtin_amdgcn_global_load_lds(sap + kb, (lds_void_ptr)&st.sa[wave * 64], 4, 0, 0);
+        if (wave < 4)
+            __builtin_amdgcn_global_load_lds(a_scales + kb + saoff, (lds_void_ptr)&st.sa[wave * 64], 4, 0, 0);
     };
+    // MFMA lane l takes row l % 16 and K group l / 16 of a piece: the uint4
+    // holding that chunk
+    const int frag = 4 * (lane & 15) + piece_chunk(lane & 15, lane >> 4);
 
     float acc[8][4][4];
 #pragma unroll
@@ -126,64 +156,94 @@ __global__ __launch_bounds__(512) void lmhead_gemm_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
+    // Per K block the wave runs 8 row groups of 4 MFMAs (one per column
+    // tile).  The partials of group mt are folded into the accumulators
+    // during group mt + 1, one column tile per MFMA, so every promotion FMA
+    // reads a result four matrix instructions old and issues while the
+    // matrix core works; the last group's promotion is carried into the next
+    // block, where it covers the wait for that block's first fragments.
+    v4f pr[2][4];
+    float f[2][4];
+    v8i af[2];
+    float4 sav[2];
+    v8i bf[4];
+
+    auto load_a = [&](const Stage& st, int mt, int slot) {
+        const uint4* As = &st.piece[0];
+        const int p = (wm * 8 + mt) * 2;
+        af[slot] = make_frag(As[p * 64 + frag], As[(p + 1) * 64 + frag]);
+        sav[slot] = *reinterpret_cast<const float4*>(&st.sa[wm * 128 + mt * 16 + 4 * (lane >> 4)]);
+    };
+    auto promote = [&](int mt, int slot, int nt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mt][nt][r] = fmaf(pr[slot][nt][r], f[slot][r], acc[mt][nt][r]);
+    };
+
+    // before the first block the carried partials are zero; the empty asm
+    // hides the zero accumulators from constant folding, so the first block
+    // compiles to the same FMAs as every other one
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) pr[1][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f[1][r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(acc[i][j][r]));
+
     auto compute = [&](const Stage& st, int kb) {
         const float sw = scalar_load(swp, kb);
-        const uint4* As = &st.piece[0];
         const uint4* Ws = &st.piece[kPieces * 64];
-        v8i bf[4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             const int p = (wn * 4 + nt) * 2;
-            bf[nt] = make_frag(Ws[p * 64 + lane], Ws[(p + 1) * 64 + lane]);
+            bf[nt] = make_frag(Ws[p * 64 + frag], Ws[(p + 1) * 64 + frag]);
         }
-        // software pipeline over the 8 row tiles: the MFMAs of row tile mt are
-        // issued before the promotion FMAs of row tile mt-1, so the matrix core
-        // and the VALU overlap while only two groups of partials are live
-        v4f pr[2][4];
-        float f[2][4];
-        auto mma = [&](int mt, int slot) {
-            const int p = (wm * 8 + mt) * 2;
-            const v8i af = make_frag(As[p * 64 + lane], As[(p + 1) * 64 + lane]);
-            const float4 sa = *reinterpret_cast<const float4*>(&st.sa[wm * 128 + mt * 16 + 4 * (lane >> 4)]);
-            f[slot][0] = sa.x * sw;
-            f[slot][1] = sa.y * sw;
-            f[slot][2] = sa.z * sw;
-            f[slot][3] = sa.w * sw;
+        load_a(st, 0, 0);
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) pr[slot][nt] = mfma_e4m3(af, bf[nt]);
-        };
-        auto promote = [&](int mt, int slot) {
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[mt][nt][r] = fmaf(pr[slot][nt][r], f[slot][r], acc[mt][nt][r]);
-        };
-        mma(0, 0);
+        for (int nt = 0; nt < 4; ++nt) promote(7, 1, nt);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mt = 1; mt < 8; ++mt) {
-            mma(mt, mt & 1);
-            promote(mt - 1, (mt - 1) & 1);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int mt = 0; mt < 8; ++mt) {
+            const int slot = mt & 1;
+            f[slot][0] = sav[slot].x * sw;
+            f[slot][1] = sav[slot].y * sw;
+            f[slot][2] = sav[slot].z * sw;
+            f[slot][3] = sav[slot].w * sw;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                pr[slot][nt] = mfma_e4m3(af[slot], bf[nt]);
+                if (mt > 0) promote(mt - 1, slot ^ 1, nt);
+                if (nt == 0 && mt < 7) load_a(st, mt + 1, slot ^ 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        promote(7, 1);
     };
 
+    // Pipeline: block kb is read from one buffer while the copy of block
+    // kb + 1 fills the other; before the barrier ending a block each wave
+    // waits for its own copies.  No branch sits between a block's FMAs and the
+    // next block (one would let the compiler sink the FMAs past it).
     copy_in(stage0, 0);
-    __syncthreads();
-    // K blocks in pairs so each half names its buffers at compile time; the
-    // copy of the next block is issued before the current block's MFMAs and
-    // the barrier that ends the block waits for it
+    MTPD_WAIT_VMCNT(0);
+    bare_barrier();
+    // K blocks in pairs so each half names its buffers at compile time
     for (int kb = 0; kb < KB; kb += 2) {
         if (kb + 1 < KB) copy_in(stage1, kb + 1);
         compute(stage0, kb);
-        __syncthreads();
+        MTPD_WAIT_VMCNT(0);
+        bare_barrier();
         if (kb + 1 < KB) {
             if (kb + 2 < KB) copy_in(stage0, kb + 2);
             compute(stage1, kb + 1);
-            __syncthreads();
+            MTPD_WAIT_VMCNT(0);
+            bare_barrier();
         }
     }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) promote(7, 1, nt);
 
     // per-row best over this wave's 64 columns, then over the four column waves
 #pragma unroll

@@ -194,7 +194,7 @@ mtpd_status mtpd_fp8_lmhead_argmax(const mtpd_qact* act, const int32_t* row_inde
                          {w->scales, (size_t)(w->V / 128) * (size_t)(w->H / 128) * 4, "w.scales"}};
     st = check_alias(outs, 3, ins, 5);
     if (st != MTPD_OK) return st;
-    mtpd::LmheadArgs a{act->codes, act->scales, row_index, n_rows, w->codes, w->scales, w->V, w->H,
+    mtpd::LmheadArgs a{act->codes, act->scales, row_index, n_rows, act->rows, w->codes, w->scales, w->V, w->H,
                        out_max, out_idx, workspace};
     return hip_status(mtpd::launch_lmhead_argmax(a, (hipStream_t)stream), "lmhead_argmax launch");
 }
@@ -229,7 +229,7 @@ mtpd_status mtpd_draft_tail(const uint16_t* hidden, const uint16_t* residual, co
                                             out_act->scales, s),
                     "norm_quant launch");
     if (st != MTPD_OK) return st;
-    mtpd::LmheadArgs a{out_act->codes, out_act->scales, nullptr, M, w->codes, w->scales, w->V, H,
+    mtpd::LmheadArgs a{out_act->codes, out_act->scales, nullptr, M, M, w->codes, w->scales, w->V, H,
                        out_max, out_idx, workspace};
     return hip_status(mtpd::launch_lmhead_argmax(a, s), "lmhead_argmax launch");
 }
