@@ -17,11 +17,17 @@ OUT_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["mtpd_api.cpp", "norm_quant.hip", "lmhead_argmax.hip", "lmhead_decode.hip", "lmhead_gemm.hip"]
+SOURCES = ["mtpd_api.cpp", "norm_quant.hip", "lmhead_argmax.hip", "lmhead_decode.hip", "lmhead_gemm.hip",
+           "lmhead_stream.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+# per-file extras: the streaming kernel keeps MFMA results in VGPRs (its
+# promotion FMAs read them at once; the AGPR form adds a copy per value)
+EXTRA = {"lmhead_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def library_path() -> str:
@@ -30,7 +36,7 @@ def library_path() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -37,6 +37,11 @@ void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len
 // the compute-regime kernel (lmhead_gemm.hip): 256 x 256 tiles, V % 256 == 0
 hipError_t launch_lmhead_gemm(const LmheadArgs& a, hipStream_t stream);
 
+// the weight-streaming kernel for one row tile (lmhead_stream.hip): n_rows <= 16
+bool stream_config_compiled(int nt, int ma, int d);
+int stream_max_h();
+hipError_t launch_lmhead_stream(const LmheadArgs& a, int nt, int ma, int d, hipStream_t stream);
+
 // the decode-regime kernel (lmhead_decode.hip): n_rows <= 64
 bool decode_config_compiled(int mt, int nt, int d);
 size_t decode_config_lds(int mt, int d, int KB);

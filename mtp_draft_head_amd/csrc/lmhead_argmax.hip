@@ -374,6 +374,35 @@ bool choose_decode(int64_t n_rows, int64_t V, int64_t H, DecodeTile* out) {
 
 }  // namespace
 
+struct StreamTile {
+    int nt, ma, d;
+};
+
+// Up to 16 rows and H <= stream_max_h(): the weight-streaming kernel, if a
+// compiled (NT, MA, D) fits (16*NT must divide V; MA eight-row activation
+// pieces; activation offsets are 32-bit).  "MTPD_LMHEAD_STREAM=nt,d"
+// overrides NT and D (tuning).
+bool use_stream(int64_t n_rows, int64_t V, int64_t H, int64_t a_rows, StreamTile* out) {
+    const char* kind = getenv("MTPD_LMHEAD_KERNEL");
+    if (kind && strcmp(kind, "generic") == 0) return false;
+    if (n_rows < 1 || n_rows > 16 || H > stream_max_h() || a_rows * H > ((int64_t)1 << 32)) return false;
+    const int ma = n_rows <= 8 ? 1 : 2;
+    StreamTile cand[3];
+    int nc = 0;
+    if (const char* e = getenv("MTPD_LMHEAD_STREAM")) {
+        StreamTile o{0, ma, 0};
+        if (sscanf(e, "%d,%d", &o.nt, &o.d) == 2) cand[nc++] = o;
+    }
+    cand[nc++] = {1, ma, 8};
+    cand[nc++] = {1, ma, 4};
+    for (int i = 0; i < nc; ++i) {
+        if (!stream_config_compiled(cand[i].nt, cand[i].ma, cand[i].d) || V % (16 * cand[i].nt)) continue;
+        *out = cand[i];
+        return true;
+    }
+    return false;
+}
+
 bool use_decode(int64_t n_rows, int64_t V, int64_t H, DecodeTile* dt) {
     const char* kind = getenv("MTPD_LMHEAD_KERNEL");   // "generic" forces the tiled kernel (testing)
     return !(kind && strcmp(kind, "generic") == 0) && choose_decode(n_rows, V, H, dt);
@@ -393,6 +422,12 @@ void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len
         snprintf(buf, len, "lmhead_gemm_kernel grid=%lldx512", (long long)((n_rows + 255) / 256 * (V / 256)));
         return;
     }
+    StreamTile st;
+    if (use_stream(n_rows, V, H, n_rows, &st)) {
+        snprintf(buf, len, "lmhead_stream_kernel<%d,%d,%d> grid=%lldx64", st.nt, st.ma, st.d,
+                 (long long)(V / (16 * st.nt)));
+        return;
+    }
     if (use_decode(n_rows, V, H, &dt)) {
         snprintf(buf, len, "lmhead_decode_kernel<%d,%d,%d> grid=%lldx256", dt.mt, dt.nt, dt.d,
                  (long long)(V / (64 * dt.nt)));
@@ -405,6 +440,8 @@ void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len
 
 hipError_t launch_lmhead_argmax(const LmheadArgs& a, hipStream_t stream) {
     if (use_gemm(a.n_rows, a.V, a.H, a.a_rows)) return launch_lmhead_gemm(a, stream);
+    StreamTile st;
+    if (use_stream(a.n_rows, a.V, a.H, a.a_rows, &st)) return launch_lmhead_stream(a, st.nt, st.ma, st.d, stream);
     DecodeTile dt;
     if (use_decode(a.n_rows, a.V, a.H, &dt))
         return launch_lmhead_decode(a, dt.mt, dt.nt, dt.d, stream);

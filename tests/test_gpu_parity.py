@@ -195,6 +195,26 @@ def test_every_launch_shape_agrees(tile, monkeypatch):
     assert torch.equal(i0, i1)
 
 
+@pytest.mark.parametrize("shape", ["1,8", "1,4", "1,12", "2,8", "2,4"])
+@pytest.mark.parametrize("M", [1, 8, 9, 16])
+def test_stream_kernel_shapes(M, shape, monkeypatch):
+    """Up to 16 rows: every weight-streaming launch shape (tiles per wave, ring
+    depth; K = 9 blocks is not a multiple of any depth) meets the oracle and
+    picks the generic kernel's indices."""
+    d = inputs.random_case(13 + M, M, 1152, 2048, outliers=True)
+    h, r, g, wc, ws = to_dev(d)
+    monkeypatch.setenv("MTPD_LMHEAD_KERNEL", "generic")
+    _, codes, scales, m0, i0 = mtpd.draft_tail(h, r, g, d["eps"], wc, ws)
+    monkeypatch.delenv("MTPD_LMHEAD_KERNEL")
+    monkeypatch.setenv("MTPD_LMHEAD_STREAM", shape)
+    say(f"  plan: {mtpd.lmhead_plan(M, 2048, 1152)}")
+    assert mtpd.lmhead_plan(M, 2048, 1152).startswith("lmhead_stream_kernel")
+    m1, i1 = mtpd.fp8_lmhead_argmax(codes, scales, wc, ws)
+    torch.cuda.synchronize()
+    check_lmhead(codes, scales, d, m1, i1)
+    assert torch.equal(i0, i1)
+
+
 @pytest.mark.parametrize("kernel", ["generic", "default"])
 def test_many_rows_both_kernels(kernel, monkeypatch):
     """More than 64 rows: the LDS-tiled 256x256 kernel by default, the generic
