@@ -42,6 +42,13 @@ bool stream_config_compiled(int nt, int ma, int d);
 int stream_max_h();
 hipError_t launch_lmhead_stream(const LmheadArgs& a, int nt, int ma, int d, hipStream_t stream);
 
+// the fused one-row draft tail (lmhead_stream.hip): M == 1, H <= 6144
+bool use_draft_tail1(int64_t M, int64_t H);
+hipError_t launch_draft_tail1(const uint16_t* hidden, const uint16_t* residual, const float* gamma, float eps,
+                              int64_t H, const uint8_t* w_codes, const float* w_scales, int64_t V,
+                              uint16_t* out_hidden, uint8_t* codes, float* scales, float* out_max, int32_t* out_idx,
+                              void* workspace, hipStream_t stream);
+
 // the decode-regime kernel (lmhead_decode.hip): n_rows <= 64
 bool decode_config_compiled(int mt, int nt, int d);
 size_t decode_config_lds(int mt, int d, int KB);

@@ -32,6 +32,9 @@
 //    into the partitioned key slots, arrival, and the last workgroup decodes
 //    (lmhead_common.h).
 
+#include <stdlib.h>
+#include <string.h>
+
 #include "kernels.h"
 #include "lmhead_common.h"
 
@@ -257,6 +260,247 @@ __global__ __launch_bounds__(64) void lmhead_stream_kernel(
     __syncthreads();
     if (!last_flag) return;
     finalize_argmax<64>(ws, n_rows, out_max, out_idx, red);
+}
+
+// ---------------------------------------------------------------------------
+// The whole draft tail for one row (decode at concurrency 1) in one kernel.
+//
+// A workgroup is four waves on one 16-row weight tile, each wave streaming a
+// quarter of the K blocks through its own ring (the streaming kernel's
+// schedule); partial accumulators meet in LDS and are summed in wave order.
+// Before that, every workgroup recomputes the row's residual add + RMSNorm +
+// E4M3 packing itself (24 KB of bf16 input plus the norm weight, L2-resident
+// after the first workgroup of each XCD), so no second launch and no
+// cross-workgroup hand-off is needed.  That part is norm_quant_kernel's body
+// for one row, thread for thread (same per-thread fma order, same butterfly,
+// same fixed-order sum of the four wave totals), so the packed row and the
+// bf16 hidden are bit-identical to the two-kernel path; the packed row stays
+// in LDS as the MFMA activation (every fragment row reads row 0) and one
+// workgroup writes the row's outputs after its stream has finished.
+// ---------------------------------------------------------------------------
+
+constexpr int kTail1MaxH = 6144;   // NSTEP <= 3: the row's inputs stay in registers
+constexpr int kTail1D = 3;         // ring depth per wave
+
+__global__ __launch_bounds__(256) void draft_tail1_kernel(
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ residual,
+    const float* __restrict__ gamma, float eps, int H,
+    const uint8_t* __restrict__ w_codes, const float* __restrict__ w_scales, int total_tiles,
+    uint16_t* __restrict__ out_hidden, uint8_t* __restrict__ codes, float* __restrict__ scales,
+    float* __restrict__ out_max, int32_t* __restrict__ out_idx, ArgmaxWs ws)
+{
+    constexpr int D = kTail1D;
+    constexpr int SLOT = 2 * 64;             // one 16-row weight tile (uint4s)
+    constexpr int PER_BLOCK = 2;
+    constexpr int NSTEP = (kTail1MaxH + 2047) / 2048;
+    __shared__ __align__(16) uint4 ring[4][D * SLOT];
+    __shared__ __align__(16) uint8_t a_lds[kTail1MaxH];
+    __shared__ __align__(16) float sa_lds[kStreamMaxKB];
+    __shared__ __align__(16) float sw_lds[4][kStreamMaxKB];
+    __shared__ float wave_sum[4];
+    __shared__ int last_flag;
+    // after the streams: wave w's partials in its own ring, the final
+    // reduction scratch in wave 0's (LDS is the occupancy limit: five
+    // workgroups per CU)
+    unsigned long long* red = reinterpret_cast<unsigned long long*>(&ring[0][0]);
+    auto part = [&](int w) { return reinterpret_cast<float*>(&ring[w][0]); };   // [4][64]
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int KB = H >> 7;
+    const int tile = xcd_contiguous((int)blockIdx.x, total_tiles);
+    const int n0 = tile * 16;
+    // this wave's K blocks [kb0, kb1), padded to whole rings
+    const int kb0 = (wave * KB) >> 2, kb1 = ((wave + 1) * KB) >> 2;
+    const int nb = kb1 - kb0;
+    const int nbp = (nb + D - 1) / D * D;
+
+    const uint8_t* wbase = w_codes + (size_t)n0 * (size_t)H;
+    uint32_t woff[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int r = 8 * q + (lane >> 3);
+        woff[q] = (uint32_t)r * (uint32_t)H + (uint32_t)ring_pos(r, lane & 7) * 16u;
+    }
+    const int fr = lane & 15, fg = lane >> 4;
+    const int fpos0 = fr * 8 + ring_pos(fr, fg);
+    const int fpos1 = fr * 8 + ring_pos(fr, fg + 4);
+    const uint32_t ring0 = lds_addr(&ring[wave][0]);
+    auto refill = [&](int j, int kb) {
+        const uint8_t* wb = wbase + (size_t)kb * kBlock;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) lds_copy16(wb, woff[q], ring0 + (uint32_t)(j * SLOT + q * 64) * 16u);
+    };
+
+    // 1. per wave: the weight-scale row and the first D blocks of its range
+    if (nb > 0) {
+        lds_copy4(w_scales + (size_t)(n0 >> 7) * KB, (uint32_t)min(lane, KB - 1) * 4u, lds_addr(&sw_lds[wave][0]));
+#pragma unroll
+        for (int j = 0; j < D; ++j) refill(j, kb0 + min(j, nb - 1));
+    }
+
+    // 2. norm_quant_kernel's body for the row (thread t owns columns
+    //    k*2048 + 8t .. +7 of each step); codes and scales go to LDS.  All
+    //    input loads (norm weight included) issue before any use: clamped
+    //    addresses, zeroed values, no branch.
+    uint4 hraw[NSTEP], rraw[NSTEP];
+    float4 graw[NSTEP][2];
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+        const int cc = min(k * 2048 + t * 8, H - 8);
+        hraw[k] = *reinterpret_cast<const uint4*>(hidden + cc);
+        rraw[k] = *reinterpret_cast<const uint4*>(residual + cc);
+        graw[k][0] = *reinterpret_cast<const float4*>(gamma + cc);
+        graw[k][1] = *reinterpret_cast<const float4*>(gamma + cc + 4);
+    }
+    asm volatile("" ::: "memory");
+    float sv[NSTEP][8];
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+        const float live = k * 2048 + t * 8 < H ? 1.f : 0.f;
+        const uint4 hv = hraw[k], rv = rraw[k];
+        sv[k][0] = (bf16_lo(hv.x) + bf16_lo(rv.x)) * live;
+        sv[k][1] = (bf16_hi(hv.x) + bf16_hi(rv.x)) * live;
+        sv[k][2] = (bf16_lo(hv.y) + bf16_lo(rv.y)) * live;
+        sv[k][3] = (bf16_hi(hv.y) + bf16_hi(rv.y)) * live;
+        sv[k][4] = (bf16_lo(hv.z) + bf16_lo(rv.z)) * live;
+        sv[k][5] = (bf16_hi(hv.z) + bf16_hi(rv.z)) * live;
+        sv[k][6] = (bf16_lo(hv.w) + bf16_lo(rv.w)) * live;
+        sv[k][7] = (bf16_hi(hv.w) + bf16_hi(rv.w)) * live;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf(sv[k][i], sv[k][i], ss);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if (lane == 0) wave_sum[wave] = ss;
+    __syncthreads();
+    const float total = (wave_sum[0] + wave_sum[1]) + (wave_sum[2] + wave_sum[3]);
+    const float rstd = (float)(1.0 / sqrt((double)total / (double)H + (double)eps));
+
+    uint4 hb[NSTEP];
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+        const int c = k * 2048 + t * 8;
+        if (c >= H) continue;   // uniform over each 16-thread scale block
+        const float4 g0 = graw[k][0], g1 = graw[k][1];
+        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        float y[8];
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            y[i] = (sv[k][i] * rstd) * g[i];
+            amax = fmaxf(amax, fabsf(y[i]));
+        }
+        hb[k].x = bf16_rne(y[0]) | (bf16_rne(y[1]) << 16);
+        hb[k].y = bf16_rne(y[2]) | (bf16_rne(y[3]) << 16);
+        hb[k].z = bf16_rne(y[4]) | (bf16_rne(y[5]) << 16);
+        hb[k].w = bf16_rne(y[6]) | (bf16_rne(y[7]) << 16);
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        const float scale = (float)((double)amax / 448.0);
+        float q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float v = scale > 0.f ? y[i] / scale : 0.f;
+            q[i] = fminf(fmaxf(v, -448.f), 448.f);
+        }
+        int lo = 0, hi = 0;
+        lo = cvt_e4m3x2<false>(q[0], q[1], lo);
+        lo = cvt_e4m3x2<true>(q[2], q[3], lo);
+        hi = cvt_e4m3x2<false>(q[4], q[5], hi);
+        hi = cvt_e4m3x2<true>(q[6], q[7], hi);
+        *reinterpret_cast<uint2*>(&a_lds[c]) = make_uint2((uint32_t)lo, (uint32_t)hi);
+        if ((t & 15) == 0) sa_lds[c >> 7] = scale;
+    }
+    __syncthreads();   // also completes every wave's ring prologue
+
+    // 3. the weight stream over this wave's blocks; fragment rows all read
+    //    the packed row
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    const float* swv = &sw_lds[wave][0];
+    auto compute = [&](int j, int i) {   // i: block index inside the range
+        const int kb = kb0 + min(i, nb - 1);
+        const float f = sa_lds[kb] * (i < nb ? swv[kb] : 0.f);
+        const uint4 a0 = *reinterpret_cast<const uint4*>(&a_lds[kb * kBlock + fg * 16]);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(&a_lds[kb * kBlock + 64 + fg * 16]);
+        const uint4* tw = &ring[wave][j * SLOT];
+        const v4f p = mfma_e4m3(make_frag(a0, a1), make_frag(tw[fpos0], tw[fpos1]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = fmaf(p[r], f, acc[r]);
+    };
+    if (nb > 0) {
+        int c = 0;
+        for (; c + D < nbp; c += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                wait_vm((D - 1) * PER_BLOCK);
+                compute(j, c + j);
+                refill(j, kb0 + min(c + D + j, nb - 1));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            wait_vm((D - 1 - j) * PER_BLOCK);
+            compute(j, c + j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // 4. partials meet in LDS, summed in wave order (row 0 sits in lanes
+    //    0..15, element 0)
+    if (wave > 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part(wave)[r * 64 + lane] = acc[r];
+    }
+    // one workgroup stores the row's outputs (every copy has completed)
+    if (tile == 0) {
+#pragma unroll
+        for (int k = 0; k < NSTEP; ++k) {
+            const int c = k * 2048 + t * 8;
+            if (c < H) {
+                *reinterpret_cast<uint4*>(out_hidden + c) = hb[k];
+                *reinterpret_cast<uint2*>(codes + c) = *reinterpret_cast<const uint2*>(&a_lds[c]);
+            }
+        }
+        if (t < KB) scales[t] = sa_lds[t];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const float z = ((acc[0] + part(1)[lane]) + part(2)[lane]) + part(3)[lane];
+        uint64_t best = argmax_key(z, (uint32_t)(n0 + (lane & 15)));
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) best = u64_max(best, shfl_xor_u64(best, off));
+        uint64_t old = 0;
+        if (lane == 0) old = merge_key(ws, 1, tile, 0, best);
+        const unsigned int dep = __builtin_amdgcn_ballot_w64(never_nonzero(old) != 0) != 0 ? 1u : 0u;
+        if (lane == 0) last_flag = arrive(ws, tile, total_tiles, dep) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    finalize_argmax<256>(ws, 1, out_max, out_idx, red);
+}
+
+bool use_draft_tail1(int64_t M, int64_t H) {
+    const char* kind = getenv("MTPD_DRAFT_TAIL");   // "split": norm_quant + LM head (testing)
+    if (kind && strcmp(kind, "split") == 0) return false;
+    return M == 1 && H <= kTail1MaxH;
+}
+
+hipError_t launch_draft_tail1(const uint16_t* hidden, const uint16_t* residual, const float* gamma, float eps,
+                              int64_t H, const uint8_t* w_codes, const float* w_scales, int64_t V,
+                              uint16_t* out_hidden, uint8_t* codes, float* scales, float* out_max, int32_t* out_idx,
+                              void* workspace, hipStream_t stream) {
+    const int64_t tiles = V / 16;
+    if (tiles > 0x7FFFFFFF || H > kTail1MaxH) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(draft_tail1_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, hidden, residual,
+                       gamma, eps, (int)H, w_codes, w_scales, (int)tiles, out_hidden, codes, scales, out_max,
+                       out_idx, argmax_ws(workspace, 1));
+    return hipGetLastError();
 }
 
 #define MTPD_STREAM_CONFIGS(X) X(1, 1, 8) X(1, 1, 4) X(1, 1, 12) X(1, 2, 8) X(1, 2, 4) X(2, 1, 8) X(2, 2, 8)

@@ -225,6 +225,11 @@ mtpd_status mtpd_draft_tail(const uint16_t* hidden, const uint16_t* residual, co
     st = check_alias(outs, 6, ins, 5);
     if (st != MTPD_OK) return st;
     const hipStream_t s = (hipStream_t)stream;
+    if (mtpd::use_draft_tail1(M, H))
+        return hip_status(mtpd::launch_draft_tail1(hidden, residual, norm_weight, eps, H, w->codes, w->scales, w->V,
+                                                   out_hidden, out_act->codes, out_act->scales, out_max, out_idx,
+                                                   workspace, s),
+                          "draft_tail launch");
     st = hip_status(mtpd::launch_norm_quant(hidden, residual, norm_weight, eps, M, H, out_hidden, out_act->codes,
                                             out_act->scales, s),
                     "norm_quant launch");

@@ -215,6 +215,25 @@ def test_stream_kernel_shapes(M, shape, monkeypatch):
     assert torch.equal(i0, i1)
 
 
+@pytest.mark.parametrize("H,V", [(128, 256), (1152, 2048), (2304, 4096), (6144, 18944)])
+def test_fused_one_row_draft_tail_matches_split(H, V, monkeypatch):
+    """One row: the fused single-kernel tail reproduces the two-launch path's
+    recycled hidden, codes and scales bit for bit (the same arithmetic), and
+    both paths' argmax meets the oracle (their K summation orders differ)."""
+    d = inputs.random_case(17 + H, 1, H, V, outliers=True)
+    h, r, g, wc, ws = to_dev(d)
+    fused = mtpd.draft_tail(h, r, g, d["eps"], wc, ws)
+    monkeypatch.setenv("MTPD_DRAFT_TAIL", "split")
+    split = mtpd.draft_tail(h, r, g, d["eps"], wc, ws)
+    torch.cuda.synchronize()
+    for x, y in zip(fused[:3], split[:3]):
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
+    check_norm_quant(d, *fused[:3])
+    check_lmhead(fused[1], fused[2], d, fused[3], fused[4])
+    check_lmhead(split[1], split[2], d, split[3], split[4])
+
+
 @pytest.mark.parametrize("kernel", ["generic", "default"])
 def test_many_rows_both_kernels(kernel, monkeypatch):
     """More than 64 rows: the LDS-tiled 256x256 kernel by default, the generic
