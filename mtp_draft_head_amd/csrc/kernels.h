@@ -42,6 +42,10 @@ bool stream_config_compiled(int nt, int ma, int d);
 int stream_max_h();
 hipError_t launch_lmhead_stream(const LmheadArgs& a, int nt, int ma, int d, hipStream_t stream);
 
+// the weight-streaming kernel with a shared activation ring (lmhead_stream.hip): n_rows <= 64
+bool rows_config_compiled(int mt, int nt, int nw, int d);
+hipError_t launch_lmhead_rows(const LmheadArgs& a, int mt, int nt, int nw, int d, hipStream_t stream);
+
 // the fused one-row draft tail (lmhead_stream.hip): M == 1, H <= 6144
 bool use_draft_tail1(int64_t M, int64_t H);
 hipError_t launch_draft_tail1(const uint16_t* hidden, const uint16_t* residual, const float* gamma, float eps,

@@ -403,6 +403,40 @@ bool use_stream(int64_t n_rows, int64_t V, int64_t H, int64_t a_rows, StreamTile
     return false;
 }
 
+struct RowsTile {
+    int mt, nt, nw, d;
+};
+
+// 17..64 rows, H <= stream_max_h(), 32-bit activation offsets: the streaming
+// kernel with a shared activation ring, if a compiled (MT, NT, NW, D) fits
+// (16*NT*NW must divide V).  "MTPD_LMHEAD_ROWS=nt,nw,d" overrides (tuning).
+bool use_rows(int64_t n_rows, int64_t V, int64_t H, int64_t a_rows, RowsTile* out) {
+    const char* kind = getenv("MTPD_LMHEAD_KERNEL");
+    if (kind && (strcmp(kind, "generic") == 0 || strcmp(kind, "decode") == 0)) return false;
+    if (n_rows <= 16 || n_rows > 64 || H > stream_max_h() || a_rows * H > ((int64_t)1 << 32)) return false;
+    const int mt = n_rows <= 32 ? 2 : 4;
+    RowsTile cand[4];
+    int nc = 0;
+    if (const char* e = getenv("MTPD_LMHEAD_ROWS")) {
+        RowsTile o{mt, 0, 0, 0};
+        if (sscanf(e, "%d,%d,%d", &o.nt, &o.nw, &o.d) == 3) cand[nc++] = o;
+    }
+    if (mt == 4) {
+        cand[nc++] = {4, 2, 4, 3};
+        cand[nc++] = {4, 1, 4, 6};
+    } else {
+        cand[nc++] = {2, 2, 4, 4};
+        cand[nc++] = {2, 1, 4, 6};
+    }
+    for (int i = 0; i < nc; ++i) {
+        const RowsTile& c = cand[i];
+        if (!rows_config_compiled(c.mt, c.nt, c.nw, c.d) || V % (16 * c.nt * c.nw)) continue;
+        *out = c;
+        return true;
+    }
+    return false;
+}
+
 bool use_decode(int64_t n_rows, int64_t V, int64_t H, DecodeTile* dt) {
     const char* kind = getenv("MTPD_LMHEAD_KERNEL");   // "generic" forces the tiled kernel (testing)
     return !(kind && strcmp(kind, "generic") == 0) && choose_decode(n_rows, V, H, dt);
@@ -428,6 +462,12 @@ void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len
                  (long long)(V / (16 * st.nt)));
         return;
     }
+    RowsTile rt;
+    if (use_rows(n_rows, V, H, n_rows, &rt)) {
+        snprintf(buf, len, "lmhead_stream_rows_kernel<%d,%d,%d,%d> grid=%lldx%d", rt.mt, rt.nt, rt.nw, rt.d,
+                 (long long)(V / (16 * rt.nt * rt.nw)), 64 * rt.nw);
+        return;
+    }
     if (use_decode(n_rows, V, H, &dt)) {
         snprintf(buf, len, "lmhead_decode_kernel<%d,%d,%d> grid=%lldx256", dt.mt, dt.nt, dt.d,
                  (long long)(V / (64 * dt.nt)));
@@ -442,6 +482,8 @@ hipError_t launch_lmhead_argmax(const LmheadArgs& a, hipStream_t stream) {
     if (use_gemm(a.n_rows, a.V, a.H, a.a_rows)) return launch_lmhead_gemm(a, stream);
     StreamTile st;
     if (use_stream(a.n_rows, a.V, a.H, a.a_rows, &st)) return launch_lmhead_stream(a, st.nt, st.ma, st.d, stream);
+    RowsTile rt;
+    if (use_rows(a.n_rows, a.V, a.H, a.a_rows, &rt)) return launch_lmhead_rows(a, rt.mt, rt.nt, rt.nw, rt.d, stream);
     DecodeTile dt;
     if (use_decode(a.n_rows, a.V, a.H, &dt))
         return launch_lmhead_decode(a, dt.mt, dt.nt, dt.d, stream);

@@ -215,6 +215,27 @@ def test_stream_kernel_shapes(M, shape, monkeypatch):
     assert torch.equal(i0, i1)
 
 
+@pytest.mark.parametrize("shape", ["2,4,4", "1,8,4", "2,4,3", "1,4,4", "1,4,3", "1,4,6"])
+@pytest.mark.parametrize("M", [17, 32, 33, 64])
+def test_stream_rows_kernel_shapes(M, shape, monkeypatch):
+    """17..64 rows: every compiled shape of the streaming kernel with a shared
+    activation ring (tiles per wave, waves, ring depth; K = 9 blocks) meets the
+    oracle and picks the decode kernel's indices."""
+    d = inputs.random_case(29 + M, M, 1152, 4096, outliers=True)
+    h, r, g, wc, ws = to_dev(d)
+    monkeypatch.setenv("MTPD_LMHEAD_KERNEL", "decode")
+    _, codes, scales, m0, i0 = mtpd.draft_tail(h, r, g, d["eps"], wc, ws)
+    monkeypatch.delenv("MTPD_LMHEAD_KERNEL")
+    monkeypatch.setenv("MTPD_LMHEAD_ROWS", shape)
+    plan = mtpd.lmhead_plan(M, 4096, 1152)
+    say(f"  plan: {plan}")
+    assert plan.startswith("lmhead_stream_rows_kernel")
+    m1, i1 = mtpd.fp8_lmhead_argmax(codes, scales, wc, ws)
+    torch.cuda.synchronize()
+    check_lmhead(codes, scales, d, m1, i1)
+    assert torch.equal(i0, i1)
+
+
 @pytest.mark.parametrize("H,V", [(128, 256), (1152, 2048), (2304, 4096), (6144, 18944)])
 def test_fused_one_row_draft_tail_matches_split(H, V, monkeypatch):
     """One row: the fused single-kernel tail reproduces the two-launch path's
