@@ -10,7 +10,10 @@ Timing: W eager warmup steps, then K steps captured in one HIP graph and
 replayed once, bracketed by device synchronizations and HIP events on the
 stream the kernels run on.  The weight is rotated over enough copies that
 the working set exceeds the 256 MB Infinity Cache.  The LM-head kernel is
-also timed alone the same way (K launches in one graph) for the roofline.
+also timed alone the same way (K launches in one graph).  The roofline is
+taken on the step's dominant kernel: the fused tail when the library runs
+the step as one kernel (then the step time is that kernel's time), else the
+LM-head kernel timed alone.
 
 Prints ONE JSON line.  --gpus above 1 is refused: this build drives one GPU.
 """
@@ -33,7 +36,8 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 MFMA
 CACHE_DEFEAT_BYTES = 768 << 20  # rotate weight copies past the 256 MB Infinity Cache
 KERNEL_SOURCES = ["mtp_draft_head_amd/csrc/lmhead_argmax.hip", "mtp_draft_head_amd/csrc/lmhead_decode.hip",
-                  "mtp_draft_head_amd/csrc/lmhead_gemm.hip",
+                  "mtp_draft_head_amd/csrc/lmhead_gemm.hip", "mtp_draft_head_amd/csrc/lmhead_stream.hip",
+                  "mtp_draft_head_amd/csrc/norm_quant.hip",
                   "mtp_draft_head_amd/csrc/lmhead_common.h", "mtp_draft_head_amd/csrc/device_common.h",
                   "mtp_draft_head_amd/csrc/kernels.h"]
 
@@ -56,10 +60,35 @@ def lmhead_bytes(M, H, V) -> int:
     return V * H + (V // 128) * (H // 128) * 4 + M * H + M * (H // 128) * 4 + M * 8
 
 
-def traffic_from_profile(workload: str):
+def tail_bytes(M, H, V) -> int:
+    """Algorithmic bytes of one fused draft-tail launch: the LM head's weight
+    codes and block scales, the rows' bf16 hidden and residual and the fp32
+    norm weight read; the bf16 recycled hidden, the packed activation (codes
+    + scales) and the (max, idx) outputs written."""
+    return V * H + (V // 128) * (H // 128) * 4 + M * H * 2 * 2 + H * 4 + M * H * 2 + M * H + M * (H // 128) * 4 + M * 8
+
+
+def dominant_kernel(M, H, V):
+    """(kernel name, 'tail' | 'lmhead', algorithmic bytes per launch) of the
+    launch that dominates a draft_tail step: the fused tail when the library
+    runs the step as one kernel, else the LM-head kernel."""
+    import mtp_draft_head_amd as mtpd
+
+    plan = mtpd.draft_tail_plan(M, V, H)
+    if "+" not in plan:
+        return plan.split()[0], "tail", tail_bytes(M, H, V), plan
+    lm = mtpd.lmhead_plan(M, V, H)
+    return lm.split("<")[0].split()[0], "lmhead", lmhead_bytes(M, H, V), lm
+
+
+def traffic_path(kernel: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+
+
+def traffic_from_profile(kernel: str, workload: str):
     """HBM bytes per launch measured by rocprofv3 counters (committed summary),
     or None when absent or taken on a different kernel source."""
-    p = os.path.join(ROOT, "profiles", f"lmhead_argmax_{workload}_traffic.json")
+    p = traffic_path(kernel, workload)
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -82,32 +111,33 @@ def _read_counters(path):
 
 
 def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, copy_mib: int) -> int:
-    """HBM bytes per LM-head launch from FETCH_SIZE / WRITE_SIZE (KiB per
-    dispatch), each scaled by the reading of the same counter for the
-    calibration copy, which reads and writes exactly copy_mib MiB.  Writes
-    profiles/lmhead_argmax_<workload>_traffic.json (and prints it)."""
+    """HBM bytes per launch of the step's dominant kernel from FETCH_SIZE /
+    WRITE_SIZE (KiB per dispatch), each scaled by the reading of the same
+    counter for the calibration copy, which reads and writes exactly
+    copy_mib MiB.  Writes profiles/<kernel>_<workload>_traffic.json (and
+    prints it)."""
     from mtp_draft_head_amd import inputs
 
     if copy_mib <= 0:
         print("--copy-calibration-mib must give the calibration copy size", file=sys.stderr)
         return 1
     w = inputs.get(workload)
-    alg = lmhead_bytes(w.M, w.H, w.V)
-    out = {"workload": workload, "kernel_hash": kernel_hash(), "algorithmic_bytes_per_launch": alg,
+    kname, _, alg, plan = dominant_kernel(w.M, w.H, w.V)
+    out = {"workload": workload, "kernel": plan, "kernel_hash": kernel_hash(), "algorithmic_bytes_per_launch": alg,
            "calibration_copy_bytes": copy_mib << 20}
     total = 0.0
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = [r for r in _read_counters(path) if r[1] == counter]
         copy = [v for k, c, v, _ in rows if "copy" in k.lower()]
-        lm = [v for k, c, v, _ in rows if "lmhead" in k]
+        lm = [v for k, c, v, _ in rows if kname in k]
         if not copy or not lm:
-            print(f"no copy or lmhead dispatches with {counter} in {path}", file=sys.stderr)
+            print(f"no copy or {kname} dispatches with {counter} in {path}", file=sys.stderr)
             return 1
         copy_kib = max(copy)                       # the calibration copy is the largest copy
         factor = (copy_mib << 20) / (copy_kib * 1024.0)
         lm_bytes = sum(lm) / len(lm) * 1024.0 * factor
         total += lm_bytes
-        out[counter] = {"lmhead_kib_per_dispatch": sum(lm) / len(lm), "lmhead_dispatches": len(lm),
+        out[counter] = {"kernel_kib_per_dispatch": sum(lm) / len(lm), "kernel_dispatches": len(lm),
                         "copy_kib": copy_kib, "scale": factor, "bytes_per_launch": lm_bytes}
     out["bytes_per_launch"] = total
     out["traffic_over_algorithmic"] = total / alg
@@ -118,7 +148,7 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, copy_mib: int) 
         f"python3 bench.py --workload {workload} --copy-calibration-mib {copy_mib} --summarize-pmc "
         f"gpurun_out/pmcf_{workload}/run_counter_collection.csv gpurun_out/pmcw_{workload}/run_counter_collection.csv",
     ]
-    dst = os.path.join(ROOT, "profiles", f"lmhead_argmax_{workload}_traffic.json")
+    dst = traffic_path(kname, workload)
     with open(dst, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
@@ -222,7 +252,10 @@ def main() -> int:
         del src, dst
 
     plan = mtpd.lmhead_plan(M, V, H)
-    log(f"[bench] LM-head plan: {plan}")
+    tail_plan = mtpd.draft_tail_plan(M, V, H)
+    kname, kind, alg, kplan = dominant_kernel(M, H, V)
+    log(f"[bench] draft_tail plan: {tail_plan}")
+    log(f"[bench] roofline kernel: {kplan} ({kind})")
     log(f"[bench] warmup {W} eager steps ({n_copies} weight copies, {n_copies * wbytes / 2**20:.0f} MiB)")
     for i in range(W):
         step(i)
@@ -271,19 +304,22 @@ def main() -> int:
     assert torch.equal(ref_idx, out[4]), "graph replay and eager call disagree"
 
     lm_us = ms_lm * 1e3
-    alg = lmhead_bytes(M, H, V)
+    lm_alg = lmhead_bytes(M, H, V)
+    # the dominant kernel: the fused tail is the whole step (one launch per
+    # step), else the LM-head kernel timed alone
+    k_us = ms_step * 1e3 if kind == "tail" else lm_us
     flops = 2.0 * M * H * V
-    gbps = alg / (lm_us * 1e-6) / 1e9
-    tflops = flops / (lm_us * 1e-6) / 1e12
+    gbps = alg / (k_us * 1e-6) / 1e9
+    tflops = flops / (k_us * 1e-6) / 1e12
     compute_bound = flops / alg > (FP8_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBPS * 1e9)
-    traffic = traffic_from_profile(w.name)
+    traffic = traffic_from_profile(kname, w.name)
     if compute_bound:
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tflops / FP8_PEAK_TFLOPS, 4), "traffic": traffic}
     else:
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
-    roof.update({"kernel": plan, "avg_launch_us": round(lm_us, 3),
+    roof.update({"kernel": kplan, "avg_launch_us": round(k_us, 3),
                  "algorithmic_bytes_per_launch": alg, "flops_per_launch": flops})
 
     cpu = None
@@ -306,8 +342,11 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "H": H, "V": V, "eps": d["eps"],
                    "weight_copies_rotated": n_copies, "timing": "K steps in one HIP graph"},
-        "lmhead": {"us": round(lm_us, 3), "GB/s": round(gbps, 1), "TFLOP/s": round(tflops, 2),
-                   "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "fp8_frac": round(tflops / FP8_PEAK_TFLOPS, 4)},
+        "draft_tail_plan": tail_plan,
+        "lmhead": {"kernel": plan, "us": round(lm_us, 3), "GB/s": round(lm_alg / (lm_us * 1e-6) / 1e9, 1),
+                   "TFLOP/s": round(flops / (lm_us * 1e-6) / 1e12, 2),
+                   "hbm_frac": round(lm_alg / (lm_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                   "fp8_frac": round(flops / (lm_us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4)},
         "eager_ms_per_step": round(eager_ms, 5),
         "roofline": roof,
         "cpu_baseline": cpu,

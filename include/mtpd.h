@@ -162,6 +162,12 @@ void mtpd_clear_error(void);
  * HIP call except a one-time query of the current device's CU count. */
 const char *mtpd_lmhead_plan(int64_t n_rows, int64_t V, int64_t H);
 
+/* Diagnostics: the kernel launches mtpd_draft_tail would make for M rows,
+ * e.g. "draft_tail1_kernel grid=1184x256" (one fused launch, M = 1) or
+ * "norm_quant_kernel<3> grid=64x256 + lmhead_stream_rows_kernel<4,2,4,3>
+ * grid=1184x256"; same string rules as mtpd_lmhead_plan. */
+const char *mtpd_draft_tail_plan(int64_t M, int64_t V, int64_t H);
+
 /* ABI version: bumped when any declaration above changes. */
 int mtpd_abi_version(void);
 

@@ -29,7 +29,7 @@ import torch
 
 __all__ = [
     "MtpdError", "MtpdLibraryMissing", "norm_quant", "fp8_lmhead_argmax", "draft_tail",
-    "workspace_bytes", "Workspace", "library_path", "lib", "lmhead_plan",
+    "workspace_bytes", "Workspace", "library_path", "lib", "lmhead_plan", "draft_tail_plan",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -98,6 +98,8 @@ def lib():
         L.mtpd_clear_error.argtypes = []
         L.mtpd_lmhead_plan.restype = ctypes.c_char_p
         L.mtpd_lmhead_plan.argtypes = [I64, I64, I64]
+        L.mtpd_draft_tail_plan.restype = ctypes.c_char_p
+        L.mtpd_draft_tail_plan.argtypes = [I64, I64, I64]
         L.mtpd_abi_version.restype = ctypes.c_int
         L.mtpd_abi_version.argtypes = []
         _lib = L
@@ -116,6 +118,11 @@ def _check(status: int):
 def lmhead_plan(n_rows: int, V: int, H: int) -> str:
     """The LM-head kernel and launch shape the library picks for these sizes."""
     return lib().mtpd_lmhead_plan(int(n_rows), int(V), int(H)).decode()
+
+
+def draft_tail_plan(M: int, V: int, H: int) -> str:
+    """The kernel launches draft_tail makes for these sizes."""
+    return lib().mtpd_draft_tail_plan(int(M), int(V), int(H)).decode()
 
 
 def workspace_bytes(n_rows: int) -> int:

@@ -132,7 +132,7 @@ const char* mtpd_last_error(void) { return g_err; }
 
 void mtpd_clear_error(void) { g_err[0] = 0; }
 
-int mtpd_abi_version(void) { return 1; }
+int mtpd_abi_version(void) { return 2; }
 
 const char* mtpd_lmhead_plan(int64_t n_rows, int64_t V, int64_t H) {
     thread_local char buf[160];
@@ -141,6 +141,23 @@ const char* mtpd_lmhead_plan(int64_t n_rows, int64_t V, int64_t H) {
         V < mtpd::kBlock || V > kMaxV || V % mtpd::kBlock)
         return buf;
     mtpd::describe_lmhead(n_rows, V, H, buf, sizeof buf);
+    return buf;
+}
+
+const char* mtpd_draft_tail_plan(int64_t M, int64_t V, int64_t H) {
+    thread_local char buf[320];
+    buf[0] = 0;
+    if (M < 1 || M > kMaxRows || H < mtpd::kBlock || H > kMaxH || H % mtpd::kBlock || V < mtpd::kBlock ||
+        V > kMaxV || V % mtpd::kBlock)
+        return buf;
+    if (mtpd::use_draft_tail1(M, H)) {
+        snprintf(buf, sizeof buf, "draft_tail1_kernel grid=%lldx256", (long long)(V / 16));
+        return buf;
+    }
+    char lm[160];
+    mtpd::describe_lmhead(M, V, H, lm, sizeof lm);
+    snprintf(buf, sizeof buf, "norm_quant_kernel<%lld> grid=%lldx256 + %s", (long long)((H + 2047) / 2048),
+             (long long)M, lm);
     return buf;
 }
 

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"mtpd_norm_quant", "mtpd_fp8_lmhead_argmax", "mtpd_draft_tail", "mtpd_workspace_bytes",
             "mtpd_status_name", "mtpd_last_error", "mtpd_clear_error", "mtpd_abi_version",
-            "mtpd_lmhead_plan"} <= set(names)
+            "mtpd_lmhead_plan", "mtpd_draft_tail_plan"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -45,7 +45,7 @@ def test_status_names_and_version(L):
         "MTPD_OK", "MTPD_ERR_NULL", "MTPD_ERR_SHAPE", "MTPD_ERR_ALIGN", "MTPD_ERR_ALIAS",
         "MTPD_ERR_WORKSPACE", "MTPD_ERR_HIP"]
     assert L.mtpd_status_name(99).decode() == "MTPD_UNKNOWN"
-    assert L.mtpd_abi_version() == 1
+    assert L.mtpd_abi_version() == 2
 
 
 def test_workspace_bytes(L):
