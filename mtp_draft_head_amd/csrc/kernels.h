@@ -44,7 +44,7 @@ hipError_t launch_lmhead_stream(const LmheadArgs& a, int nt, int ma, int d, hipS
 
 // the weight-streaming kernel with a shared activation ring (lmhead_stream.hip): n_rows <= 64
 bool rows_config_compiled(int mt, int nt, int nw, int d);
-hipError_t launch_lmhead_rows(const LmheadArgs& a, int mt, int nt, int nw, int d, hipStream_t stream);
+hipError_t launch_lmhead_rows(const LmheadArgs& a, int mt, int nt, int nw, int d, int cus, hipStream_t stream);
 
 // the fused one-row draft tail (lmhead_stream.hip): M == 1, H <= 6144
 bool use_draft_tail1(int64_t M, int64_t H);

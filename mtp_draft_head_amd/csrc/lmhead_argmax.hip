@@ -38,6 +38,7 @@
 // V*H code bytes + V*H/16384*4 scale bytes per call.
 
 #include <stdio.h>
+#include <algorithm>
 #include <stdlib.h>
 #include <string.h>
 
@@ -464,8 +465,10 @@ void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len
     }
     RowsTile rt;
     if (use_rows(n_rows, V, H, n_rows, &rt)) {
-        snprintf(buf, len, "lmhead_stream_rows_kernel<%d,%d,%d,%d> grid=%lldx%d", rt.mt, rt.nt, rt.nw, rt.d,
-                 (long long)(V / (16 * rt.nt * rt.nw)), 64 * rt.nw);
+        const long long tiles = (long long)(V / (16 * rt.nt * rt.nw));
+        const long long grid = std::max<long long>(std::min<long long>(tiles, device_cus()), (tiles + 15) / 16);
+        snprintf(buf, len, "lmhead_stream_rows_kernel<%d,%d,%d,%d> grid=%lldx%d (%lld tiles)", rt.mt, rt.nt,
+                 rt.nw, rt.d, grid, 64 * rt.nw, tiles);
         return;
     }
     if (use_decode(n_rows, V, H, &dt)) {
@@ -483,7 +486,8 @@ hipError_t launch_lmhead_argmax(const LmheadArgs& a, hipStream_t stream) {
     StreamTile st;
     if (use_stream(a.n_rows, a.V, a.H, a.a_rows, &st)) return launch_lmhead_stream(a, st.nt, st.ma, st.d, stream);
     RowsTile rt;
-    if (use_rows(a.n_rows, a.V, a.H, a.a_rows, &rt)) return launch_lmhead_rows(a, rt.mt, rt.nt, rt.nw, rt.d, stream);
+    if (use_rows(a.n_rows, a.V, a.H, a.a_rows, &rt))
+        return launch_lmhead_rows(a, rt.mt, rt.nt, rt.nw, rt.d, device_cus(), stream);
     DecodeTile dt;
     if (use_decode(a.n_rows, a.V, a.H, &dt))
         return launch_lmhead_decode(a, dt.mt, dt.nt, dt.d, stream);

@@ -35,6 +35,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "kernels.h"
 #include "lmhead_common.h"
 
@@ -265,17 +267,35 @@ __global__ __launch_bounds__(64) void lmhead_stream_kernel(
 // ---------------------------------------------------------------------------
 // 17..64 activation rows: the same weight stream, with the activation shared.
 //
-// A workgroup is NW waves; each wave owns NT 16-row weight tiles and keeps
-// its own weight ring (as above).  The activation block (MT*16 rows x 128
-// bytes) is needed by every wave, so it lives in one workgroup ring of the
-// same depth, each wave copying 2*MT/NW of its 8-row pieces.  Per block a
-// wave waits for its own copies of that block, then a barrier makes every
-// wave's pieces visible; past the barrier all waves have finished the
-// previous block, so its slot (activation and weight) is refilled with the
-// block D-1 ahead.  Activation scales of all rows are copied into LDS once.
-// Epilogue: per-row best keys of the NW waves meet in LDS, one merge per
-// row, arrival, and the last workgroup decodes.
+// A workgroup is NW waves and stays resident: it takes weight tiles
+// t = blockIdx, blockIdx + G, ... (NW*NT*16 vocab rows each), and all its
+// tiles' K blocks form one continuous stream, so the rings never drain
+// between tiles.  Each wave keeps its own weight ring (as above); the
+// activation block (MT*16 rows x 128 bytes) is needed by every wave, so it
+// lives in one workgroup ring of the same depth, each wave copying 2*MT/NW of
+// its 8-row pieces.  Per block a wave waits for its own copies of that block,
+// then a barrier makes every wave's pieces visible; past the barrier all
+// waves have finished the previous block, so its slot (activation and
+// weight) is refilled with the block D-1 ahead.  The activation scales of all
+// rows and the weight-scale rows of all the workgroup's tiles are copied into
+// LDS once, before the stream.  At the end of each tile the wave folds its
+// per-row best keys into a running maximum in LDS (all tiles share the same
+// activation rows); at the end the NW waves' maxima meet, one merge per row,
+// arrival, and the last workgroup decodes.
 // ---------------------------------------------------------------------------
+
+constexpr int kRowsMaxTilesPerWg = 16;   // weight-scale rows staged per workgroup
+constexpr size_t kLdsPerWorkgroup = 160 * 1024;   // gfx950
+
+// LDS of a rows-kernel shape: the static arrays plus the activation-scale
+// table at its largest (H = kStreamMaxH).
+constexpr size_t rows_lds_bytes(int mt, int nt, int nw, int d) {
+    return (size_t)nw * d * nt * 2 * 64 * 16      // weight rings
+           + (size_t)d * mt * 2 * 64 * 16         // activation ring
+           + (size_t)kRowsMaxTilesPerWg * kStreamMaxKB * 4
+           + (size_t)64 * nw * 8 + 64             // running maxima, flag, alignment
+           + (size_t)mt * 16 * kStreamMaxKB * 4;  // activation-scale table
+}
 
 template <int MT, int NT, int NW, int D>
 __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
@@ -287,36 +307,39 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
     ArgmaxWs ws)
 {
     constexpr int ROWS = MT * 16;
+    constexpr int TROWS = NW * NT * 16;      // vocab rows per tile
     constexpr int WSLOT = NT * 2 * 64;       // uint4s per wave per block
     constexpr int ASLOT = MT * 2 * 64;       // uint4s per activation block
     constexpr int APW = 2 * MT / NW;         // activation pieces each wave copies per block
     static_assert(APW * NW == 2 * MT, "activation pieces must split evenly over the waves");
-    constexpr int SPW = ROWS / NW;           // activation-scale rows each wave copies per block
-    constexpr int PER_BLOCK = 2 * NT + APW + 1;
+    constexpr int PER_BLOCK = 2 * NT + APW;
     static_assert((D - 2) * PER_BLOCK <= 63, "vmcnt holds at most 63");
+    static_assert(TROWS <= 128 && 128 % TROWS == 0, "a tile sits inside one weight-scale block");
+    static_assert(rows_lds_bytes(MT, NT, NW, D) <= kLdsPerWorkgroup, "shape exceeds the LDS of a workgroup");
     __shared__ __align__(16) uint4 wring[NW][D * WSLOT];
     __shared__ __align__(16) uint4 aring[D * ASLOT];
-    __shared__ __align__(16) float sring[D][64];   // activation scales of each ring block
-    __shared__ __align__(16) float sw_lds[NW][kStreamMaxKB];
-    __shared__ unsigned long long red[64 * NW];
+    __shared__ __align__(16) float sw_lds[kRowsMaxTilesPerWg][kStreamMaxKB];
+    __shared__ unsigned long long red[64 * NW];   // running per-row maxima, one set per wave
     __shared__ int last_flag;
+    extern __shared__ __align__(16) float sa_lds[];   // [ROWS][KB]
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int KB = H >> 7;
-    const int tile = xcd_contiguous((int)blockIdx.x, total_tiles);
-    const int n0 = tile * (NW * NT * 16) + wave * (NT * 16);   // this wave's first vocab row
+    const int G = (int)gridDim.x;
+    const int b = (int)blockIdx.x;
+    const int ntiles = (total_tiles - b + G - 1) / G;   // this workgroup's tiles: b, b+G, ...
+    const int nunits = ntiles * KB;
 
-    // weight copies (as in lmhead_stream_kernel)
-    const uint8_t* wbase = w_codes + (size_t)n0 * (size_t)H;
     uint32_t woff[NT][2];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int r = 8 * q + (lane >> 3);
-            woff[nt][q] = (uint32_t)(nt * 16 + r) * (uint32_t)H + (uint32_t)ring_pos(r, lane & 7) * 16u;
+            woff[nt][q] = (uint32_t)(wave * NT * 16 + nt * 16 + r) * (uint32_t)H +
+                          (uint32_t)ring_pos(r, lane & 7) * 16u;
         }
     // activation copies: piece p = wave + NW*i covers rows 8p..8p+7 (row tile
     // p/2, half p%2), clamped to the last row
@@ -324,41 +347,65 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
 #pragma unroll
     for (int i = 0; i < APW; ++i) {
         const int p = wave + NW * i;
-        const int r16 = 8 * (p & 1) + (lane >> 3);          // row inside its 16-row tile
+        const int r16 = 8 * (p & 1) + (lane >> 3);
         const int m = min(8 * p + (lane >> 3), n_rows - 1);
         aoff[i] = (uint32_t)(row_index ? row_index[m] : m) * (uint32_t)H + (uint32_t)ring_pos(r16, lane & 7) * 16u;
     }
-    // activation-scale copy: lane l < SPW of wave w takes row w*SPW + l (one
-    // dword per row per block; lanes past SPW idle)
-    uint32_t soff;
-    {
-        const int m = min(wave * SPW + min(lane, SPW - 1), n_rows - 1);
-        soff = (uint32_t)(row_index ? row_index[m] : m) * (uint32_t)KB * 4u;
+    // activation-scale rows this wave copies, loaded (and waited for) before
+    // any copy is issued
+    constexpr int RPW = ROWS / NW;
+    uint32_t srow[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int m = min(wave * RPW + i, n_rows - 1);
+        srow[i] = (uint32_t)(row_index ? row_index[m] : m);
     }
+    MTPD_WAIT_VM(0);
+    asm volatile("" ::: "memory");
+
     const int fr = lane & 15, fg = lane >> 4;
     const int fpos0 = fr * 8 + ring_pos(fr, fg);
     const int fpos1 = fr * 8 + ring_pos(fr, fg + 4);
     const uint32_t wring0 = lds_addr(&wring[wave][0]);
     const uint32_t aring0 = lds_addr(aring);
-    const uint32_t sring0 = lds_addr(sring);
 
-    auto refill = [&](int j, int kb) {
-        const uint8_t* wb = wbase + (size_t)kb * kBlock;
+    // unit u = (tile index i, block kb); refills walk the units with their
+    // own counters (clamped to the last unit)
+    auto refill = [&](int j, int i, int kb) {
+        const int tile = b + i * G;
+        const uint8_t* wb = w_codes + (size_t)tile * TROWS * (size_t)H + (size_t)kb * kBlock;
         const uint8_t* ab = a_codes + (size_t)kb * kBlock;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int q = 0; q < 2; ++q) lds_copy16(wb, woff[nt][q], wring0 + (uint32_t)(j * WSLOT + (nt * 2 + q) * 64) * 16u);
 #pragma unroll
-        for (int i = 0; i < APW; ++i)
-            lds_copy16(ab, aoff[i], aring0 + (uint32_t)(j * ASLOT + (wave + NW * i) * 64) * 16u);
-        if (lane < SPW) lds_copy4(a_scales + kb, soff, sring0 + (uint32_t)(j * 64 + wave * SPW) * 4u);
+        for (int i2 = 0; i2 < APW; ++i2)
+            lds_copy16(ab, aoff[i2], aring0 + (uint32_t)(j * ASLOT + (wave + NW * i2) * 64) * 16u);
     };
 
-    // prologue: this wave's weight-scale row, then blocks 0..D-2
-    lds_copy4(w_scales + (size_t)(n0 >> 7) * KB, (uint32_t)min(lane, KB - 1) * 4u, lds_addr(&sw_lds[wave][0]));
+    // prologue: scale tables (lanes past KB idle), then units 0..D-2
+    if (lane < KB) {
 #pragma unroll
-    for (int j = 0; j < D - 1; ++j) refill(j, min(j, KB - 1));
+        for (int i = 0; i < RPW; ++i)
+            lds_copy4(a_scales, (srow[i] * (uint32_t)KB + (uint32_t)lane) * 4u, lds_addr(&sa_lds[(wave * RPW + i) * KB]));
+        for (int i = wave; i < ntiles; i += NW)
+            lds_copy4(w_scales + (size_t)((b + i * G) * TROWS >> 7) * KB, (uint32_t)lane * 4u, lds_addr(&sw_lds[i][0]));
+    }
+    if (lane < ROWS) red[wave * 64 + lane] = 0;
+    int ri = 0, rkb = 0;   // next unit to request
+    auto next_req = [&]() {
+        const int i = ri, kb = rkb;
+        if (ri * KB + rkb < nunits - 1) {
+            if (++rkb == KB) { rkb = 0; ++ri; }
+        }
+        return make_int2(i, kb);
+    };
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) {
+        const int2 u = next_req();
+        refill(j, u.x, u.y);
+    }
 
     float acc[MT][NT][4];
 #pragma unroll
@@ -368,11 +415,9 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[mt][nt][i] = 0.f;
 
-    const float* swv = &sw_lds[wave][0];
-    auto compute = [&](int j, int kb) {
-        const int kc = min(kb, KB - 1);
-        const float swl = swv[kc];
-        const float sw = kb < KB ? swl : 0.f;
+    auto compute = [&](int j, int i, int kb, bool live) {
+        const float swl = sw_lds[i][kb];
+        const float sw = live ? swl : 0.f;
         const uint4* tw = &wring[wave][j * WSLOT];
         v8i bf[NT];
 #pragma unroll
@@ -381,8 +426,8 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
         for (int mt = 0; mt < MT; ++mt) {
             const uint4* ta = &aring[j * ASLOT + mt * 128];
             const v8i af = make_frag(ta[fpos0], ta[fpos1]);
-            const float4 sa = *reinterpret_cast<const float4*>(&sring[j][mt * 16 + 4 * fg]);
-            const float f0 = sa.x * sw, f1 = sa.y * sw, f2 = sa.z * sw, f3 = sa.w * sw;
+            const float* sr = &sa_lds[(mt * 16 + 4 * fg) * KB + kb];
+            const float f0 = sr[0] * sw, f1 = sr[KB] * sw, f2 = sr[2 * KB] * sw, f3 = sr[3 * KB] * sw;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const v4f p = mfma_e4m3(af, bf[nt]);
@@ -393,56 +438,70 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
             }
         }
     };
+    // a finished tile: per-row best over this wave's columns, folded into the
+    // wave's running maxima; the accumulators restart
+    auto fold = [&](int i) {
+        const int n0 = (b + i * G) * TROWS + wave * NT * 16;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint64_t best = 0;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    best = u64_max(best, argmax_key(acc[mt][nt][r], (uint32_t)(n0 + nt * 16 + (lane & 15))));
+                    acc[mt][nt][r] = 0.f;
+                }
+#pragma unroll
+                for (int off = 8; off > 0; off >>= 1) best = u64_max(best, shfl_xor_u64(best, off));
+                if ((lane & 15) == 0) {
+                    unsigned long long* slot = &red[wave * 64 + mt * 16 + 4 * (lane >> 4) + r];
+                    *slot = u64_max(*slot, best);
+                }
+            }
+    };
 
-    // blocks in rounds of D so slot numbers are compile-time; padding blocks
-    // (kb >= KB) get a zero weight-scale factor
-    const int KBp = (KB + D - 1) / D * D;
-    int c = 0;
-    for (; c < KBp; c += D) {
+    // units in rounds of D so ring slots are compile-time; the last round is
+    // padded with repeats of the last unit (zero weight-scale factor)
+    int ci = 0, ckb = 0;   // unit being consumed
+    const int nup = (nunits + D - 1) / D * D;
+    for (int c = 0; c < nup; c += D) {
 #pragma unroll
         for (int j = 0; j < D; ++j) {
-            wait_vm((D - 2) * PER_BLOCK);   // this wave's copies of block c + j
-            __builtin_amdgcn_s_barrier();   // everyone's; and everyone is past block c + j - 1
+            wait_vm((D - 2) * PER_BLOCK);   // this wave's copies of this unit
+            __builtin_amdgcn_s_barrier();   // everyone's; and everyone is past the previous unit
             asm volatile("" ::: "memory");
-            refill((j + D - 1) % D, min(c + j + D - 1, KB - 1));
-            compute(j, c + j);
+            {
+                const int2 u = next_req();
+                refill((j + D - 1) % D, u.x, u.y);
+            }
+            const bool live = c + j < nunits;
+            compute(j, ci, ckb, live);
+            if (live && ckb == KB - 1) fold(ci);
+            if (live && ++ckb == KB) { ckb = 0; ++ci; }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
     MTPD_WAIT_VM(0);   // the clamped tail refills, before LDS is reused
-
-    // per-row best over this wave's columns, then over the NW waves
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint64_t best = 0;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                best = u64_max(best, argmax_key(acc[mt][nt][i], (uint32_t)(n0 + nt * 16 + (lane & 15))));
-#pragma unroll
-            for (int off = 8; off > 0; off >>= 1) best = u64_max(best, shfl_xor_u64(best, off));
-            if ((lane & 15) == 0) red[wave * 64 + mt * 16 + 4 * (lane >> 4) + i] = best;
-        }
-    }
     __syncthreads();
+
     if (wave == 0) {
         uint64_t old = 0;
         if (lane < ROWS && lane < n_rows) {
             uint64_t k = red[lane];
 #pragma unroll
             for (int w = 1; w < NW; ++w) k = u64_max(k, red[w * 64 + lane]);
-            old = merge_key(ws, n_rows, tile, lane, k);
+            old = merge_key(ws, n_rows, b, lane, k);
         }
         const unsigned int dep = __builtin_amdgcn_ballot_w64(never_nonzero(old) != 0) != 0 ? 1u : 0u;
-        if (lane == 0) last_flag = arrive(ws, tile, total_tiles, dep) ? 1 : 0;
+        if (lane == 0) last_flag = arrive(ws, b, G, dep) ? 1 : 0;
     }
     __syncthreads();
     if (!last_flag) return;
     finalize_argmax<64 * NW>(ws, n_rows, out_max, out_idx, red);
 }
 
-#define MTPD_ROWS_CONFIGS(X) X(4, 2, 4, 4) X(4, 1, 8, 4) X(4, 2, 4, 3) X(4, 1, 4, 4) X(4, 1, 4, 3) X(2, 2, 4, 4) X(2, 1, 4, 6) X(2, 1, 4, 4) X(4, 1, 4, 6)
+#define MTPD_ROWS_CONFIGS(X) X(4, 2, 4, 4) X(4, 2, 4, 5) X(4, 1, 8, 4) X(4, 2, 4, 3) X(4, 1, 4, 4) X(4, 1, 4, 3) X(2, 2, 4, 4) X(2, 2, 4, 6) X(2, 1, 4, 6) X(2, 1, 4, 4) X(4, 1, 4, 6)
 
 bool rows_config_compiled(int mt, int nt, int nw, int d) {
 #define MTPD_X(a, b, c2, e) if (mt == a && nt == b && nw == c2 && d == e) return true;
@@ -451,15 +510,32 @@ bool rows_config_compiled(int mt, int nt, int nw, int d) {
     return false;
 }
 
-hipError_t launch_lmhead_rows(const LmheadArgs& a, int mt, int nt, int nw, int d, hipStream_t stream) {
+hipError_t launch_lmhead_rows(const LmheadArgs& a, int mt, int nt, int nw, int d, int cus, hipStream_t stream) {
     const int64_t tiles = a.V / (16 * nt * nw);
     if (tiles > 0x7FFFFFFF || a.H > kStreamMaxH || a.n_rows > 16 * mt) return hipErrorInvalidValue;
-#define MTPD_X(p, q, r, u)                                                                                   \
-    if (mt == p && nt == q && nw == r && d == u) {                                                          \
-        hipLaunchKernelGGL((lmhead_stream_rows_kernel<p, q, r, u>), dim3((unsigned)tiles), dim3(64 * r), 0,   \
-                           stream, a.a_codes, a.a_scales, a.row_index, (int)a.n_rows, a.w_codes, a.w_scales, \
-                           (int)a.H, (int)tiles, a.out_max, a.out_idx, argmax_ws(a.workspace, a.n_rows));   \
-        return hipGetLastError();                                                                           \
+    // one resident workgroup per CU, at most kRowsMaxTilesPerWg tiles each
+    int64_t grid = std::min<int64_t>(tiles, cus);
+    grid = std::max<int64_t>(grid, (tiles + kRowsMaxTilesPerWg - 1) / kRowsMaxTilesPerWg);
+    const size_t lds = (size_t)(16 * mt) * (size_t)(a.H / kBlock) * sizeof(float);
+    // never dispatch a shape whose LDS (static + the scale table) does not fit
+    // a workgroup: the dispatch would be rejected by the device
+    auto fits = [&](const void* kernel) {
+        hipFuncAttributes attr;
+        if (hipFuncGetAttributes(&attr, kernel) != hipSuccess) return false;
+        int dev = 0, cap = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cap, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            return false;
+        return attr.sharedSizeBytes + lds <= (size_t)cap;
+    };
+#define MTPD_X(p, q, r, u)                                                                                    \
+    if (mt == p && nt == q && nw == r && d == u) {                                                           \
+        if (!fits(reinterpret_cast<const void*>(&lmhead_stream_rows_kernel<p, q, r, u>)))                   \
+            return hipErrorInvalidConfiguration;                                                             \
+        hipLaunchKernelGGL((lmhead_stream_rows_kernel<p, q, r, u>), dim3((unsigned)grid), dim3(64 * r), lds,  \
+                           stream, a.a_codes, a.a_scales, a.row_index, (int)a.n_rows, a.w_codes, a.w_scales,  \
+                           (int)a.H, (int)tiles, a.out_max, a.out_idx, argmax_ws(a.workspace, a.n_rows));    \
+        return hipGetLastError();                                                                            \
     }
     MTPD_ROWS_CONFIGS(MTPD_X)
 #undef MTPD_X
