@@ -15,6 +15,18 @@ taken on the step's dominant kernel: the fused tail when the library runs
 the step as one kernel (then the step time is that kernel's time), else the
 LM-head kernel timed alone.
 
+Variants (--variant), each the same path computed another way, for the
+steps next to it under tensor parallelism, on one GPU's share:
+  tail           the step above (default)
+  vocab_shards   norm_quant, then the LM head as 8 vocab-shard launches
+                 (V/8 rows each) whose local (max, index) pairs one
+                 argmax_combine launch reduces to the global draft token;
+                 roofline on one shard launch
+  allreduce_tail allreduce_norm_quant over 8 row-parallel bf16 partials
+                 (standing in for the peers' outputs) + the LM head;
+                 roofline on the all-reduce + norm kernel (the partial sets
+                 are rotated past the Infinity Cache too)
+
 Prints ONE JSON line.  --gpus above 1 is refused: this build drives one GPU.
 """
 from __future__ import annotations
@@ -35,21 +47,26 @@ METRIC = "draft rows/s + LM-head HBM GB/s (% of peak) for fused norm-quant-FP8-G
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 MFMA
 CACHE_DEFEAT_BYTES = 768 << 20  # rotate weight copies past the 256 MB Infinity Cache
-KERNEL_SOURCES = ["mtp_draft_head_amd/csrc/lmhead_argmax.hip", "mtp_draft_head_amd/csrc/lmhead_decode.hip",
-                  "mtp_draft_head_amd/csrc/lmhead_gemm.hip", "mtp_draft_head_amd/csrc/lmhead_stream.hip",
-                  "mtp_draft_head_amd/csrc/norm_quant.hip",
-                  "mtp_draft_head_amd/csrc/lmhead_common.h", "mtp_draft_head_amd/csrc/device_common.h",
-                  "mtp_draft_head_amd/csrc/kernels.h"]
+CSRC = "mtp_draft_head_amd/csrc/"
+# the source a kernel is defined in; a traffic summary stays valid while that
+# file and the shared headers are unchanged
+KERNEL_SOURCE = {"lmhead_gemm_kernel": "lmhead_gemm.hip", "lmhead_decode_kernel": "lmhead_decode.hip",
+                 "lmhead_argmax_kernel": "lmhead_argmax.hip", "lmhead_stream_kernel": "lmhead_stream.hip",
+                 "lmhead_stream_rows_kernel": "lmhead_stream.hip", "draft_tail1_kernel": "lmhead_stream.hip",
+                 "allreduce_norm_quant_kernel": "norm_quant.hip", "norm_quant_kernel": "norm_quant.hip",
+                 "argmax_combine_kernel": "argmax_combine.hip"}
+SHARED_HEADERS = ["lmhead_common.h", "device_common.h", "kernels.h"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash() -> str:
+def kernel_hash(kernel: str) -> str:
+    """Digest of the kernel's own source file and the shared headers."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
+    for name in [KERNEL_SOURCE.get(kernel, "lmhead_argmax.hip")] + SHARED_HEADERS:
+        with open(os.path.join(ROOT, CSRC + name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -81,19 +98,47 @@ def dominant_kernel(M, H, V):
     return lm.split("<")[0].split()[0], "lmhead", lmhead_bytes(M, H, V), lm
 
 
-def traffic_path(kernel: str, workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+N_SHARDS = 8      # vocab shards of the vocab_shards variant
+N_PARTIALS = 8    # row-parallel partials of the allreduce_tail variant
 
 
-def traffic_from_profile(kernel: str, workload: str):
+def allreduce_norm_bytes(P, M, H) -> int:
+    """Algorithmic bytes of one allreduce_norm_quant launch: P partials and the
+    residual read (bf16), the fp32 norm weight read once; the bf16 recycled
+    hidden, the codes and the scales written."""
+    return 2 * M * H * (P + 1) + 4 * H + 2 * M * H + M * H + M * (H // 128) * 4
+
+
+def roofline_kernel(variant, M, H, V):
+    """(kernel name, kind, algorithmic bytes per launch, plan, flops per launch)
+    of the kernel a variant's roofline is taken on."""
+    import mtp_draft_head_amd as mtpd
+
+    if variant == "vocab_shards":
+        Vs = V // N_SHARDS
+        plan = mtpd.lmhead_plan(M, Vs, H)
+        return plan.split("<")[0].split()[0], "lmhead", lmhead_bytes(M, H, Vs), plan, 2.0 * M * H * Vs
+    if variant == "allreduce_tail":
+        name = "allreduce_norm_quant_kernel"
+        return name, "norm", allreduce_norm_bytes(N_PARTIALS, M, H), f"{name} grid={M}x256 P={N_PARTIALS}", 0.0
+    kname, kind, alg, plan = dominant_kernel(M, H, V)
+    return kname, kind, alg, plan, 2.0 * M * H * V
+
+
+def traffic_path(kernel: str, workload: str, variant: str = "tail") -> str:
+    tag = workload if variant == "tail" else f"{workload}_{variant}"
+    return os.path.join(ROOT, "profiles", f"{kernel}_{tag}_traffic.json")
+
+
+def traffic_from_profile(kernel: str, workload: str, variant: str = "tail"):
     """HBM bytes per launch measured by rocprofv3 counters (committed summary),
     or None when absent or taken on a different kernel source."""
-    p = traffic_path(kernel, workload)
+    p = traffic_path(kernel, workload, variant)
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("kernel_hash") != kernel_hash():
+    if t.get("kernel_hash") != kernel_hash(kernel):
         return None
     return t.get("bytes_per_launch")
 
@@ -110,7 +155,7 @@ def _read_counters(path):
     return rows
 
 
-def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, copy_mib: int) -> int:
+def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, copy_mib: int, variant: str = "tail") -> int:
     """HBM bytes per launch of the step's dominant kernel from FETCH_SIZE /
     WRITE_SIZE (KiB per dispatch), each scaled by the reading of the same
     counter for the calibration copy, which reads and writes exactly
@@ -122,8 +167,9 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, copy_mib: int) 
         print("--copy-calibration-mib must give the calibration copy size", file=sys.stderr)
         return 1
     w = inputs.get(workload)
-    kname, _, alg, plan = dominant_kernel(w.M, w.H, w.V)
-    out = {"workload": workload, "kernel": plan, "kernel_hash": kernel_hash(), "algorithmic_bytes_per_launch": alg,
+    kname, _, alg, plan, _ = roofline_kernel(variant, w.M, w.H, w.V)
+    out = {"workload": workload, "variant": variant, "kernel": plan, "kernel_hash": kernel_hash(kname),
+           "algorithmic_bytes_per_launch": alg,
            "calibration_copy_bytes": copy_mib << 20}
     total = 0.0
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -141,24 +187,28 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, copy_mib: int) 
                         "copy_kib": copy_kib, "scale": factor, "bytes_per_launch": lm_bytes}
     out["bytes_per_launch"] = total
     out["traffic_over_algorithmic"] = total / alg
-    run = f"python3 bench.py --no-cpu-baseline --workload {workload} --steps 20 --warmup 5 --copy-calibration-mib {copy_mib}"
+    vflag = "" if variant == "tail" else f" --variant {variant}"
+    tag = workload if variant == "tail" else f"{workload}_{variant}"
+    run = (f"python3 bench.py --no-cpu-baseline --workload {workload}{vflag} --steps 20 --warmup 5 "
+           f"--copy-calibration-mib {copy_mib}")
     out["commands"] = [
-        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcf_{workload} -o run -- {run}",
-        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcw_{workload} -o run -- {run}",
-        f"python3 bench.py --workload {workload} --copy-calibration-mib {copy_mib} --summarize-pmc "
-        f"gpurun_out/pmcf_{workload}/run_counter_collection.csv gpurun_out/pmcw_{workload}/run_counter_collection.csv",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcf_{tag} -o run -- {run}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcw_{tag} -o run -- {run}",
+        f"python3 bench.py --workload {workload}{vflag} --copy-calibration-mib {copy_mib} --summarize-pmc "
+        f"gpurun_out/pmcf_{tag}/run_counter_collection.csv gpurun_out/pmcw_{tag}/run_counter_collection.csv",
     ]
-    dst = traffic_path(kname, workload)
+    dst = traffic_path(kname, workload, variant)
     with open(dst, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
     return 0
 
 
-def cpu_baseline(d, seconds: float):
+def cpu_baseline(d, seconds: float, variant: str = "tail", parts=None):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    the full tail (norm + pack + LM head + argmax) for n rows drawn cyclically
-    from the workload's rows, n sized to take about `seconds`."""
+    the variant's full tail (norm + pack + LM head + argmax, with the partial
+    sum or the shard combine where the variant has one) for n rows drawn
+    cyclically from the workload's rows, n sized to take about `seconds`."""
     import numpy as np
 
     import oracle
@@ -169,15 +219,23 @@ def cpu_baseline(d, seconds: float):
     def run(n):
         rows = np.arange(n) % w.M
         t0 = time.perf_counter()
-        nq = oracle.norm_quant(d["hidden"][rows], d["residual"][rows], d["norm_weight"], d["eps"])
-        oracle.argmax(nq["codes"], nq["scales"], d["w_codes"], d["w_scales"])
+        if variant == "allreduce_tail":
+            nq = oracle.allreduce_norm_quant(parts[:, rows], d["residual"][rows], d["norm_weight"], d["eps"])
+        else:
+            nq = oracle.norm_quant(d["hidden"][rows], d["residual"][rows], d["norm_weight"], d["eps"])
+        if variant == "vocab_shards":
+            oracle.argmax_sharded(nq["codes"], nq["scales"], d["w_codes"], d["w_scales"], V // N_SHARDS)
+        else:
+            oracle.argmax(nq["codes"], nq["scales"], d["w_codes"], d["w_scales"])
         return time.perf_counter() - t0
 
     t1 = run(1)
     n = max(1, min(4096, int(seconds / max(t1, 1e-4))))
     t = run(n)
+    what = {"tail": "full tail", "vocab_shards": f"full tail with {N_SHARDS} vocab shards combined",
+            "allreduce_tail": f"full tail with the {N_PARTIALS}-partial sum"}[variant]
     return {"value": n / t, "unit": "rows/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{n} rows of {w.name} (M={w.M} H={H} V={V}, rows taken cyclically), full tail "
+            "sample": f"{n} rows of {w.name} (M={w.M} H={H} V={V}, rows taken cyclically), {what} "
                       f"incl. the whole {V}-row LM head per row, fp64, {t:.1f} s"}
 
 
@@ -187,16 +245,17 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_c1_tp8_shard")
+    ap.add_argument("--variant", default="tail", choices=["tail", "vocab_shards", "allreduce_tail"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (a counter reference for PMC runs)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a run with "
-                         "--copy-calibration-mib into the LM-head traffic summary under profiles/")
+                         "--copy-calibration-mib into the traffic summary under profiles/")
     args = ap.parse_args()
     if args.summarize_pmc:
-        return summarize_pmc(args.workload, *args.summarize_pmc, args.copy_calibration_mib)
+        return summarize_pmc(args.workload, *args.summarize_pmc, args.copy_calibration_mib, args.variant)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py drives exactly one GPU: the multi-GPU path (vocab shards combined by a u64 max "
@@ -209,11 +268,15 @@ def main() -> int:
     import mtp_draft_head_amd as mtpd
     from mtp_draft_head_amd import inputs
 
+    variant = args.variant
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     w = inputs.get(args.workload)
     M, H, V = w.M, w.H, w.V
-    log(f"[bench] drawing workload {w.name}: M={M} H={H} V={V}")
+    if variant == "vocab_shards" and V % (N_SHARDS * 128):
+        print(f"{w.name}: V={V} does not split into {N_SHARDS} shards of whole 128-row blocks", file=sys.stderr)
+        return 2
+    log(f"[bench] drawing workload {w.name}: M={M} H={H} V={V} (variant {variant})")
     d = inputs.make(w.name)
 
     hid = torch.from_numpy(d["hidden"].view(np.int16)).to(dev).view(torch.bfloat16)
@@ -234,12 +297,52 @@ def main() -> int:
     wsp = mtpd.Workspace(dev)
     wsp.get(M)
     K, W = args.steps, args.warmup
+    extra = {}
 
-    def step(i):
-        mtpd.draft_tail(hid, res, g, d["eps"], wcs[i % n_copies], wss[i % n_copies], workspace=wsp, out=out)
+    parts_np = None
+    if variant == "tail":
+        def step(i):
+            mtpd.draft_tail(hid, res, g, d["eps"], wcs[i % n_copies], wss[i % n_copies], workspace=wsp, out=out)
 
-    def lm_step(i):
-        mtpd.fp8_lmhead_argmax(out[1], out[2], wcs[i % n_copies], wss[i % n_copies], workspace=wsp, out=lm_out)
+        def kernel_step(i):
+            mtpd.fp8_lmhead_argmax(out[1], out[2], wcs[i % n_copies], wss[i % n_copies], workspace=wsp, out=lm_out)
+    elif variant == "vocab_shards":
+        S = V // N_SHARDS
+        offs = [k * S for k in range(N_SHARDS)]
+        shards = [[(wcs[c][k * S:(k + 1) * S], wss[c][k * S // 128:(k + 1) * S // 128]) for k in range(N_SHARDS)]
+                  for c in range(n_copies)]
+        lmax = torch.empty((N_SHARDS, M), dtype=torch.float32, device=dev)
+        lidx = torch.empty((N_SHARDS, M), dtype=torch.int32, device=dev)
+
+        def step(i):
+            mtpd.norm_quant(hid, res, g, d["eps"], out=out[:3])
+            for k, (c, sc) in enumerate(shards[i % n_copies]):
+                mtpd.fp8_lmhead_argmax(out[1], out[2], c, sc, workspace=wsp, out=(lmax[k], lidx[k]))
+            mtpd.argmax_combine(lmax, lidx, offs, out=(out[3], out[4]))
+
+        def kernel_step(i):
+            c, sc = shards[(i // N_SHARDS) % n_copies][i % N_SHARDS]
+            mtpd.fp8_lmhead_argmax(out[1], out[2], c, sc, workspace=wsp, out=lm_out)
+
+        def combine_step(i):
+            mtpd.argmax_combine(lmax, lidx, offs, out=lm_out)
+    else:
+        parts_np = inputs.partials(w.name, N_PARTIALS)
+        pset = [torch.from_numpy(parts_np[p].view(np.int16)).to(dev).view(torch.bfloat16) for p in range(N_PARTIALS)]
+        n_sets = max(1, math.ceil(CACHE_DEFEAT_BYTES / (N_PARTIALS * M * H * 2)))
+        psets = [pset] + [[t.clone() for t in pset] for _ in range(n_sets - 1)]
+        extra["partial_sets_rotated"] = n_sets
+
+        def step(i):
+            mtpd.allreduce_norm_quant(psets[i % n_sets], res, g, d["eps"], out=out[:3])
+            mtpd.fp8_lmhead_argmax(out[1], out[2], wcs[i % n_copies], wss[i % n_copies], workspace=wsp,
+                                   out=(out[3], out[4]))
+
+        def kernel_step(i):
+            mtpd.allreduce_norm_quant(psets[i % n_sets], res, g, d["eps"], out=out[:3])
+
+        def lm_alone(i):
+            mtpd.fp8_lmhead_argmax(out[1], out[2], wcs[i % n_copies], wss[i % n_copies], workspace=wsp, out=lm_out)
 
     if args.copy_calibration_mib:
         nb = args.copy_calibration_mib << 20
@@ -253,8 +356,9 @@ def main() -> int:
 
     plan = mtpd.lmhead_plan(M, V, H)
     tail_plan = mtpd.draft_tail_plan(M, V, H)
-    kname, kind, alg, kplan = dominant_kernel(M, H, V)
-    log(f"[bench] draft_tail plan: {tail_plan}")
+    kname, kind, alg, kplan, kflops = roofline_kernel(variant, M, H, V)
+    if variant == "tail":
+        log(f"[bench] draft_tail plan: {tail_plan}")
     log(f"[bench] roofline kernel: {kplan} ({kind})")
     log(f"[bench] warmup {W} eager steps ({n_copies} weight copies, {n_copies * wbytes / 2**20:.0f} MiB)")
     for i in range(W):
@@ -290,11 +394,18 @@ def main() -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / K, graph
 
-    log(f"[bench] timing {K} draft_tail steps (one HIP graph)")
+    log(f"[bench] timing {K} steps (one HIP graph)")
     ms_step, g1 = timed_graph(step)
-    log(f"[bench] timing {K} LM-head launches (one HIP graph)")
-    ms_lm, g2 = timed_graph(lm_step)
+    log(f"[bench] timing {K} launches of the roofline kernel (one HIP graph)")
+    ms_kernel, g2 = timed_graph(kernel_step)
     del g1, g2
+    if variant == "vocab_shards":
+        ms_comb, g3 = timed_graph(combine_step)
+        del g3
+        extra["argmax_combine_us"] = round(ms_comb * 1e3, 3)
+    if variant == "allreduce_tail":
+        ms_lm_alone, g3 = timed_graph(lm_alone)
+        del g3
 
     # sanity: the timed outputs are the real ones
     torch.cuda.synchronize()
@@ -303,16 +414,14 @@ def main() -> int:
     torch.cuda.synchronize()
     assert torch.equal(ref_idx, out[4]), "graph replay and eager call disagree"
 
-    lm_us = ms_lm * 1e3
-    lm_alg = lmhead_bytes(M, H, V)
-    # the dominant kernel: the fused tail is the whole step (one launch per
-    # step), else the LM-head kernel timed alone
-    k_us = ms_step * 1e3 if kind == "tail" else lm_us
     flops = 2.0 * M * H * V
+    # the roofline kernel's time: the fused tail is the whole step (one launch
+    # per step); otherwise the kernel timed alone
+    k_us = ms_step * 1e3 if kind == "tail" else ms_kernel * 1e3
     gbps = alg / (k_us * 1e-6) / 1e9
-    tflops = flops / (k_us * 1e-6) / 1e12
-    compute_bound = flops / alg > (FP8_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBPS * 1e9)
-    traffic = traffic_from_profile(kname, w.name)
+    tflops = kflops / (k_us * 1e-6) / 1e12
+    compute_bound = kflops / alg > (FP8_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBPS * 1e9)
+    traffic = traffic_from_profile(kname, w.name, variant)
     if compute_bound:
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tflops / FP8_PEAK_TFLOPS, 4), "traffic": traffic}
@@ -320,13 +429,28 @@ def main() -> int:
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
     roof.update({"kernel": kplan, "avg_launch_us": round(k_us, 3),
-                 "algorithmic_bytes_per_launch": alg, "flops_per_launch": flops})
+                 "algorithmic_bytes_per_launch": alg, "flops_per_launch": kflops})
+
+    # the full-vocab LM head alone (the tail's second launch), for reference
+    if variant == "tail":
+        lm_us = ms_kernel * 1e3
+    elif variant == "allreduce_tail":
+        lm_us = ms_lm_alone * 1e3
+    else:
+        lm_us = None
+    lm_alg = lmhead_bytes(M, H, V)
 
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle (~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(d, args.cpu_seconds)
+        cpu = cpu_baseline(d, args.cpu_seconds, variant, parts_np)
 
+    config = {"workload": w.name, "M": M, "H": H, "V": V, "eps": d["eps"],
+              "weight_copies_rotated": n_copies, "timing": "K steps in one HIP graph"}
+    if variant != "tail":
+        config["variant"] = variant
+        config["shards" if variant == "vocab_shards" else "partials"] = (
+            N_SHARDS if variant == "vocab_shards" else N_PARTIALS)
     rec = {
         "metric": METRIC,
         "value": round(M / (ms_step * 1e-3), 1),
@@ -340,17 +464,17 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "fp8_e4m3",
         "data": "synthetic",
-        "config": {"workload": w.name, "M": M, "H": H, "V": V, "eps": d["eps"],
-                   "weight_copies_rotated": n_copies, "timing": "K steps in one HIP graph"},
-        "draft_tail_plan": tail_plan,
-        "lmhead": {"kernel": plan, "us": round(lm_us, 3), "GB/s": round(lm_alg / (lm_us * 1e-6) / 1e9, 1),
-                   "TFLOP/s": round(flops / (lm_us * 1e-6) / 1e12, 2),
-                   "hbm_frac": round(lm_alg / (lm_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-                   "fp8_frac": round(flops / (lm_us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4)},
-        "eager_ms_per_step": round(eager_ms, 5),
-        "roofline": roof,
-        "cpu_baseline": cpu,
+        "config": config,
     }
+    if variant == "tail":
+        rec["draft_tail_plan"] = tail_plan
+    if lm_us is not None:
+        rec["lmhead"] = {"kernel": plan, "us": round(lm_us, 3), "GB/s": round(lm_alg / (lm_us * 1e-6) / 1e9, 1),
+                         "TFLOP/s": round(flops / (lm_us * 1e-6) / 1e12, 2),
+                         "hbm_frac": round(lm_alg / (lm_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "fp8_frac": round(flops / (lm_us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4)}
+    rec.update(extra)
+    rec.update({"eager_ms_per_step": round(eager_ms, 5), "roofline": roof, "cpu_baseline": cpu})
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -143,6 +143,53 @@ mtpd_status mtpd_draft_tail(const uint16_t *hidden, const uint16_t *residual,
                             float *out_max, int32_t *out_idx,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * mtpd_norm_quant with the MTP layer's trailing all-reduce folded in
+ * ("Fuse the MTP trailing all-reduce; local-argmax draft tokens", Summary:
+ * all-reduce and RMSNorm as one fused step; Accuracy: fp32 accumulation).
+ * The norm input is the sum of the row-parallel partial outputs of the
+ * layer's last projection plus the residual:
+ *
+ *   s = f32(partials[0]) + f32(partials[1]) + ... + f32(partials[P-1])
+ *       + f32(residual)      accumulated in fp32, left to right
+ *
+ * and everything after s is exactly mtpd_norm_quant's (same outputs, same
+ * rounding); with n_partials == 1 the results are bit-identical to
+ * mtpd_norm_quant(partials[0], residual, ...).
+ *
+ * partials: a HOST array of n_partials device pointers, each [M][H] bf16 (on
+ * one GPU they stand in for the peers' buffers a one-shot all-reduce reads;
+ * moving data between GPUs is not part of this call).  1 <= n_partials <= 16.
+ * The other arguments are mtpd_norm_quant's; no output may overlap a partial.
+ */
+mtpd_status mtpd_allreduce_norm_quant(const uint16_t *const *partials, int64_t n_partials,
+                                      const uint16_t *residual, const float *norm_weight, float eps,
+                                      int64_t M, int64_t H, uint16_t *out_hidden, const mtpd_qact *out_act,
+                                      void *stream);
+
+/*
+ * Vocab-parallel combine of per-shard greedy argmaxes
+ * ("Fuse the MTP trailing all-reduce; local-argmax draft tokens", Summary:
+ * each GPU's local argmax over its vocab slice replaces the gather of
+ * full-vocab logits).  Shard s covers global vocab rows shard_offset[s] ..
+ * and returned local pairs (local_max[s][i], local_idx[s][i]) from
+ * mtpd_fp8_lmhead_argmax.  For each row i:
+ *   out_idx[i] = the lowest global index shard_offset[s] + local_idx[s][i]
+ *                among the shards whose local_max[s][i] is the largest
+ *                (+0 and -0 compare equal);
+ *   out_max[i] = that maximum (-0 is returned as +0).
+ * When the shards tile [0, V) this equals the full-vocab greedy argmax.
+ *
+ * local_max: [n_shards][n_rows] f32, local_idx: [n_shards][n_rows] int32,
+ * device memory, row-major.  shard_offset: HOST array of n_shards values in
+ * [0, 2^31 - 128]; every offset + local index must stay below 2^31 (not
+ * checked on the device).  out_max: [n_rows] f32, out_idx: [n_rows] int32.
+ * 1 <= n_shards <= 64; n_rows == 0 launches nothing.  No workspace.
+ */
+mtpd_status mtpd_argmax_combine(const float *local_max, const int32_t *local_idx,
+                                const int64_t *shard_offset, int64_t n_shards, int64_t n_rows,
+                                float *out_max, int32_t *out_idx, void *stream);
+
 /* Bytes of workspace mtpd_fp8_lmhead_argmax / mtpd_draft_tail need for
  * n_rows output rows (a multiple of 256; 0 for n_rows <= 0). */
 size_t mtpd_workspace_bytes(int64_t n_rows);

@@ -18,6 +18,10 @@ Entry points (same names as the C ABI):
       -> (max f32 [n], idx int32 [n])
   draft_tail(hidden, residual, norm_weight, eps, w_codes, w_scales)
       -> (out_hidden, codes, scales, max, idx)
+  allreduce_norm_quant(partials, residual, norm_weight, eps)
+      -> norm_quant's outputs for the norm input sum(partials) + residual
+  argmax_combine(local_max, local_idx, shard_offsets)
+      -> (max f32 [n], global idx int32 [n]) from per-shard pairs [P, n]
 """
 from __future__ import annotations
 
@@ -30,6 +34,7 @@ import torch
 __all__ = [
     "MtpdError", "MtpdLibraryMissing", "norm_quant", "fp8_lmhead_argmax", "draft_tail",
     "workspace_bytes", "Workspace", "library_path", "lib", "lmhead_plan", "draft_tail_plan",
+    "allreduce_norm_quant", "argmax_combine",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -88,6 +93,11 @@ def lib():
         L.mtpd_draft_tail.restype = ctypes.c_int
         L.mtpd_draft_tail.argtypes = [P, P, P, F, I64, I64, ctypes.POINTER(FP8Weight), P,
                                       ctypes.POINTER(QAct), P, P, P, ctypes.c_size_t, P]
+        L.mtpd_allreduce_norm_quant.restype = ctypes.c_int
+        L.mtpd_allreduce_norm_quant.argtypes = [ctypes.POINTER(ctypes.c_void_p), I64, P, P, F, I64, I64, P,
+                                                ctypes.POINTER(QAct), P]
+        L.mtpd_argmax_combine.restype = ctypes.c_int
+        L.mtpd_argmax_combine.argtypes = [P, P, ctypes.POINTER(ctypes.c_int64), I64, I64, P, P, P]
         L.mtpd_workspace_bytes.restype = ctypes.c_size_t
         L.mtpd_workspace_bytes.argtypes = [I64]
         L.mtpd_status_name.restype = ctypes.c_char_p
@@ -262,3 +272,62 @@ def draft_tail(hidden, residual, norm_weight, eps, w_codes, w_scales, workspace:
                                      out_max.data_ptr(), out_idx.data_ptr(), ws.data_ptr(), ws.numel(),
                                      _stream(dev)))
     return out_h, codes, scales, out_max, out_idx
+
+
+def allreduce_norm_quant(partials, residual, norm_weight, eps: float = 1e-6, out=None):
+    """norm_quant whose norm input is sum(partials) + residual (fp32, in list order).
+
+    partials: a sequence of 1..16 bf16 [M,H] device tensors (the row-parallel
+    partial outputs an all-reduce would sum).  Returns (out_hidden, codes, scales).
+    """
+    parts = list(partials)
+    if not parts:
+        raise ValueError("at least one partial is required")
+    for i, p in enumerate(parts):
+        _dev(p, f"partials[{i}]", _BF16, 2)
+        if p.shape != parts[0].shape or p.device != parts[0].device:
+            raise ValueError("partials must share shape and device")
+    _dev(residual, "residual", _BF16, 2)
+    _dev(norm_weight, "norm_weight", (torch.float32,), 1)
+    M, H = residual.shape
+    dev = residual.device
+    if out is None:
+        out_h = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        codes = torch.empty((M, H), dtype=torch.uint8, device=dev)
+        scales = torch.empty((M, H // BLOCK if H % BLOCK == 0 else 0), dtype=torch.float32, device=dev)
+    else:
+        out_h, codes, scales = out
+    ptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
+    qa = QAct(codes.data_ptr(), scales.data_ptr(), M, H)
+    with torch.cuda.device(dev):
+        _check(lib().mtpd_allreduce_norm_quant(ptrs, len(parts), residual.data_ptr(), norm_weight.data_ptr(),
+                                               float(eps), M, H, out_h.data_ptr(), ctypes.byref(qa), _stream(dev)))
+    return out_h, codes, scales
+
+
+def argmax_combine(local_max, local_idx, shard_offsets, out=None):
+    """Global greedy argmax from per-shard local pairs.
+
+    local_max float32 [P, n], local_idx int32 [P, n] (device); shard_offsets:
+    P ints, the first global vocab row of each shard.  Returns (max float32 [n],
+    idx int32 [n]) with global indices.
+    """
+    _dev(local_max, "local_max", (torch.float32,), 2)
+    _dev(local_idx, "local_idx", (torch.int32,), 2)
+    if local_max.shape != local_idx.shape:
+        raise ValueError("local_max and local_idx differ in shape")
+    P, n = local_max.shape
+    offs = [int(o) for o in shard_offsets]
+    if len(offs) != P:
+        raise ValueError(f"{len(offs)} shard offsets for {P} shards")
+    dev = local_max.device
+    if out is None:
+        out_max = torch.empty((n,), dtype=torch.float32, device=dev)
+        out_idx = torch.empty((n,), dtype=torch.int32, device=dev)
+    else:
+        out_max, out_idx = out
+    arr = (ctypes.c_int64 * max(P, 1))(*offs)
+    with torch.cuda.device(dev):
+        _check(lib().mtpd_argmax_combine(local_max.data_ptr(), local_idx.data_ptr(), arr, P, n,
+                                         out_max.data_ptr(), out_idx.data_ptr(), _stream(dev)))
+    return out_max, out_idx

@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["mtpd_api.cpp", "norm_quant.hip", "lmhead_argmax.hip", "lmhead_decode.hip", "lmhead_gemm.hip",
-           "lmhead_stream.hip"]
+           "lmhead_stream.hip", "argmax_combine.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -14,6 +14,29 @@ hipError_t launch_norm_quant(const uint16_t* hidden, const uint16_t* residual, c
                              float eps, int64_t M, int64_t H, uint16_t* out_hidden, uint8_t* codes,
                              float* scales, hipStream_t stream);
 
+// Row-parallel partial outputs summed by allreduce_norm_quant_kernel: n
+// device pointers, each [M][H] bf16 (passed by value as a kernel argument).
+constexpr int kMaxPartials = 16;
+struct PartialPtrs {
+    const uint16_t* p[kMaxPartials];
+    int n;
+};
+
+hipError_t launch_allreduce_norm_quant(const PartialPtrs& parts, const uint16_t* residual, const float* gamma,
+                                       float eps, int64_t M, int64_t H, uint16_t* out_hidden, uint8_t* codes,
+                                       float* scales, hipStream_t stream);
+
+// Vocab-parallel combine of per-shard (max, local index) pairs
+// (argmax_combine.hip): offsets by value, at most kMaxShards shards.
+constexpr int kMaxShards = 64;
+struct ShardOffsets {
+    uint32_t off[kMaxShards];
+};
+
+hipError_t launch_argmax_combine(const float* local_max, const int32_t* local_idx, const ShardOffsets& offs,
+                                 int n_shards, int64_t n_rows, float* out_max, int32_t* out_idx,
+                                 hipStream_t stream);
+
 struct LmheadArgs {
     const uint8_t* a_codes;
     const float* a_scales;

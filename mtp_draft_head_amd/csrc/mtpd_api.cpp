@@ -132,7 +132,7 @@ const char* mtpd_last_error(void) { return g_err; }
 
 void mtpd_clear_error(void) { g_err[0] = 0; }
 
-int mtpd_abi_version(void) { return 2; }
+int mtpd_abi_version(void) { return 3; }
 
 const char* mtpd_lmhead_plan(int64_t n_rows, int64_t V, int64_t H) {
     thread_local char buf[160];
@@ -254,6 +254,63 @@ mtpd_status mtpd_draft_tail(const uint16_t* hidden, const uint16_t* residual, co
     mtpd::LmheadArgs a{out_act->codes, out_act->scales, nullptr, M, M, w->codes, w->scales, w->V, H,
                        out_max, out_idx, workspace};
     return hip_status(mtpd::launch_lmhead_argmax(a, s), "lmhead_argmax launch");
+}
+
+mtpd_status mtpd_allreduce_norm_quant(const uint16_t* const* partials, int64_t n_partials, const uint16_t* residual,
+                                      const float* norm_weight, float eps, int64_t M, int64_t H, uint16_t* out_hidden,
+                                      const mtpd_qact* out_act, void* stream) {
+    if (n_partials < 1 || n_partials > mtpd::kMaxPartials)
+        return fail(MTPD_ERR_SHAPE, "n_partials=%lld out of [1, %d]", (long long)n_partials, mtpd::kMaxPartials);
+    if (!partials) return fail(MTPD_ERR_NULL, "partials array is NULL");
+    mtpd_status st = check_norm_args(partials[0], residual, norm_weight, M, H, out_hidden, out_act);
+    if (st != MTPD_OK || M == 0) return st;
+    const size_t mh = (size_t)M * (size_t)H;
+    mtpd::PartialPtrs parts{};
+    parts.n = (int)n_partials;
+    Range ins[mtpd::kMaxPartials + 2];
+    for (int64_t q = 0; q < n_partials; ++q) {
+        if (!partials[q]) return fail(MTPD_ERR_NULL, "partials[%lld] is NULL", (long long)q);
+        if (!aligned(partials[q], 16)) return fail(MTPD_ERR_ALIGN, "partials[%lld] not 16-byte aligned", (long long)q);
+        parts.p[q] = partials[q];
+        ins[q] = Range{partials[q], mh * 2, "a partial"};
+    }
+    ins[n_partials] = Range{residual, mh * 2, "residual"};
+    ins[n_partials + 1] = Range{norm_weight, (size_t)H * 4, "norm_weight"};
+    const Range outs[] = {{out_hidden, mh * 2, "out_hidden"},
+                          {out_act->codes, mh, "out_act.codes"},
+                          {out_act->scales, mh / 128 * 4, "out_act.scales"}};
+    st = check_alias(outs, 3, ins, (int)n_partials + 2);
+    if (st != MTPD_OK) return st;
+    return hip_status(mtpd::launch_allreduce_norm_quant(parts, residual, norm_weight, eps, M, H, out_hidden,
+                                                        out_act->codes, out_act->scales, (hipStream_t)stream),
+                      "allreduce_norm_quant launch");
+}
+
+mtpd_status mtpd_argmax_combine(const float* local_max, const int32_t* local_idx, const int64_t* shard_offset,
+                                int64_t n_shards, int64_t n_rows, float* out_max, int32_t* out_idx, void* stream) {
+    if (n_shards < 1 || n_shards > mtpd::kMaxShards)
+        return fail(MTPD_ERR_SHAPE, "n_shards=%lld out of [1, %d]", (long long)n_shards, mtpd::kMaxShards);
+    if (n_rows < 0 || n_rows > kMaxRows) return fail(MTPD_ERR_SHAPE, "n_rows=%lld out of [0, 2^24]", (long long)n_rows);
+    if (!shard_offset) return fail(MTPD_ERR_NULL, "shard_offset is NULL");
+    mtpd::ShardOffsets offs{};
+    for (int64_t s = 0; s < n_shards; ++s) {
+        if (shard_offset[s] < 0 || shard_offset[s] > kMaxV)
+            return fail(MTPD_ERR_SHAPE, "shard_offset[%lld]=%lld out of [0, 2^31-128]", (long long)s,
+                        (long long)shard_offset[s]);
+        offs.off[s] = (uint32_t)shard_offset[s];
+    }
+    if (n_rows == 0) return MTPD_OK;
+    if (!local_max || !local_idx || !out_max || !out_idx) return fail(MTPD_ERR_NULL, "a required pointer is NULL");
+    if (!aligned(local_max, 4) || !aligned(local_idx, 4) || !aligned(out_max, 4) || !aligned(out_idx, 4))
+        return fail(MTPD_ERR_ALIGN, "max/index arrays must be 4-byte aligned");
+    const size_t pairs = (size_t)n_shards * (size_t)n_rows;
+    const Range outs[] = {{out_max, (size_t)n_rows * 4, "out_max"}, {out_idx, (size_t)n_rows * 4, "out_idx"}};
+    const Range ins[] = {{local_max, pairs * 4, "local_max"}, {local_idx, pairs * 4, "local_idx"}};
+    mtpd_status st = check_alias(outs, 2, ins, 2);
+    if (st != MTPD_OK) return st;
+    return hip_status(mtpd::launch_argmax_combine(local_max, local_idx, offs, (int)n_shards, n_rows, out_max, out_idx,
+                                                  (hipStream_t)stream),
+                      "argmax_combine launch");
 }
 
 }  // extern "C"

@@ -25,37 +25,17 @@
 
 namespace mtpd {
 
+// The norm and the two outputs for one row, from the fp32 norm input s held
+// in registers (thread t owns columns step*2048 + 8t .. +7; zero past H).
 template <int NSTEP>
-__global__ __launch_bounds__(256) void norm_quant_kernel(
-    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ residual,
-    const float* __restrict__ gamma, float eps, int H,
-    uint16_t* __restrict__ out_hidden, uint8_t* __restrict__ codes, float* __restrict__ scales)
+__device__ __forceinline__ void norm_quant_finish(const float (&s)[NSTEP][8], const float* __restrict__ gamma,
+                                                  float eps, int H, size_t row, float* wave_sum,
+                                                  uint16_t* __restrict__ out_hidden, uint8_t* __restrict__ codes,
+                                                  float* __restrict__ scales)
 {
-    __shared__ float wave_sum[4];
     const int t = threadIdx.x;
-    const size_t base = (size_t)blockIdx.x * (size_t)H;
+    const size_t base = row * (size_t)H;
     const int KB = H >> 7;
-
-    float s[NSTEP][8];
-#pragma unroll
-    for (int k = 0; k < NSTEP; ++k) {
-        const int c = k * 2048 + t * 8;
-        if (c < H) {
-            const uint4 hv = *reinterpret_cast<const uint4*>(hidden + base + c);
-            const uint4 rv = *reinterpret_cast<const uint4*>(residual + base + c);
-            s[k][0] = bf16_lo(hv.x) + bf16_lo(rv.x);
-            s[k][1] = bf16_hi(hv.x) + bf16_hi(rv.x);
-            s[k][2] = bf16_lo(hv.y) + bf16_lo(rv.y);
-            s[k][3] = bf16_hi(hv.y) + bf16_hi(rv.y);
-            s[k][4] = bf16_lo(hv.z) + bf16_lo(rv.z);
-            s[k][5] = bf16_hi(hv.z) + bf16_hi(rv.z);
-            s[k][6] = bf16_lo(hv.w) + bf16_lo(rv.w);
-            s[k][7] = bf16_hi(hv.w) + bf16_hi(rv.w);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) s[k][i] = 0.f;
-        }
-    }
 
     float ss = 0.f;
 #pragma unroll
@@ -107,8 +87,114 @@ __global__ __launch_bounds__(256) void norm_quant_kernel(
         hi = cvt_e4m3x2<false>(q[4], q[5], hi);
         hi = cvt_e4m3x2<true>(q[6], q[7], hi);
         *reinterpret_cast<uint2*>(codes + base + c) = make_uint2((uint32_t)lo, (uint32_t)hi);
-        if ((t & 15) == 0) scales[(size_t)blockIdx.x * KB + (c >> 7)] = scale;
+        if ((t & 15) == 0) scales[row * KB + (c >> 7)] = scale;
     }
+}
+
+// Adds the 8 bf16 values of v to s (fp32, one rounding per element).
+__device__ __forceinline__ void add_bf16x8(float (&s)[8], const uint4 v) {
+    s[0] += bf16_lo(v.x);
+    s[1] += bf16_hi(v.x);
+    s[2] += bf16_lo(v.y);
+    s[3] += bf16_hi(v.y);
+    s[4] += bf16_lo(v.z);
+    s[5] += bf16_hi(v.z);
+    s[6] += bf16_lo(v.w);
+    s[7] += bf16_hi(v.w);
+}
+
+template <int NSTEP>
+__global__ __launch_bounds__(256) void norm_quant_kernel(
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ residual,
+    const float* __restrict__ gamma, float eps, int H,
+    uint16_t* __restrict__ out_hidden, uint8_t* __restrict__ codes, float* __restrict__ scales)
+{
+    __shared__ float wave_sum[4];
+    const int t = threadIdx.x;
+    const size_t base = (size_t)blockIdx.x * (size_t)H;
+
+    float s[NSTEP][8];
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+        const int c = k * 2048 + t * 8;
+        if (c < H) {
+            const uint4 hv = *reinterpret_cast<const uint4*>(hidden + base + c);
+            const uint4 rv = *reinterpret_cast<const uint4*>(residual + base + c);
+            s[k][0] = bf16_lo(hv.x) + bf16_lo(rv.x);
+            s[k][1] = bf16_hi(hv.x) + bf16_hi(rv.x);
+            s[k][2] = bf16_lo(hv.y) + bf16_lo(rv.y);
+            s[k][3] = bf16_hi(hv.y) + bf16_hi(rv.y);
+            s[k][4] = bf16_lo(hv.z) + bf16_lo(rv.z);
+            s[k][5] = bf16_hi(hv.z) + bf16_hi(rv.z);
+            s[k][6] = bf16_lo(hv.w) + bf16_lo(rv.w);
+            s[k][7] = bf16_hi(hv.w) + bf16_hi(rv.w);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s[k][i] = 0.f;
+        }
+    }
+    norm_quant_finish<NSTEP>(s, gamma, eps, H, blockIdx.x, wave_sum, out_hidden, codes, scales);
+}
+
+// ---------------------------------------------------------------------------
+// The same step with the MTP layer's trailing all-reduce folded in: the norm
+// input is the sum of P row-parallel partial outputs plus the residual
+// ("[Spec Decode][Perf] Fuse the MTP trailing all-reduce; local-argmax draft
+// tokens", Summary: the all-reduce and the RMSNorm run as one fused step;
+// Accuracy: fp32 accumulation).  Here the P partials are device buffers on
+// this GPU standing in for the peers' outputs (a one-shot all-reduce reads
+// each peer's buffer once); the transport between GPUs is not part of it.
+//
+//   s = ((p_0 + p_1) + ... + p_{P-1}) + residual      fp32, in partial order
+//
+// PMAX >= P loads are issued per 2048-column step before any add (addresses
+// of partials past P repeat partial 0 and their values are not added), so a
+// row's whole input is in flight at once.  With P == 1 the result is
+// bit-identical to norm_quant_kernel on (p_0, residual).
+//
+// Bytes per row: 2H (P + 1) read + 4H of norm weight (cache-resident) +
+// 3H + H/32 written.
+// ---------------------------------------------------------------------------
+
+template <int NSTEP, int PMAX>
+__global__ __launch_bounds__(256) void allreduce_norm_quant_kernel(
+    PartialPtrs parts, const uint16_t* __restrict__ residual,
+    const float* __restrict__ gamma, float eps, int H,
+    uint16_t* __restrict__ out_hidden, uint8_t* __restrict__ codes, float* __restrict__ scales)
+{
+    __shared__ float wave_sum[4];
+    const int t = threadIdx.x;
+    const size_t base = (size_t)blockIdx.x * (size_t)H;
+    const int P = parts.n;
+
+    float s[NSTEP][8];
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+        const int c = k * 2048 + t * 8;
+        if (c < H) {
+            uint4 pv[PMAX];
+#pragma unroll
+            for (int q = 0; q < PMAX; ++q)
+                pv[q] = *reinterpret_cast<const uint4*>(parts.p[q < P ? q : 0] + base + c);
+            const uint4 rv = *reinterpret_cast<const uint4*>(residual + base + c);
+            s[k][0] = bf16_lo(pv[0].x);
+            s[k][1] = bf16_hi(pv[0].x);
+            s[k][2] = bf16_lo(pv[0].y);
+            s[k][3] = bf16_hi(pv[0].y);
+            s[k][4] = bf16_lo(pv[0].z);
+            s[k][5] = bf16_hi(pv[0].z);
+            s[k][6] = bf16_lo(pv[0].w);
+            s[k][7] = bf16_hi(pv[0].w);
+#pragma unroll
+            for (int q = 1; q < PMAX; ++q)
+                if (q < P) add_bf16x8(s[k], pv[q]);
+            add_bf16x8(s[k], rv);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s[k][i] = 0.f;
+        }
+    }
+    norm_quant_finish<NSTEP>(s, gamma, eps, H, blockIdx.x, wave_sum, out_hidden, codes, scales);
 }
 
 hipError_t launch_norm_quant(const uint16_t* hidden, const uint16_t* residual, const float* gamma,
@@ -136,6 +222,36 @@ hipError_t launch_norm_quant(const uint16_t* hidden, const uint16_t* residual, c
     }
 #undef MTPD_NQ_CASE
     return hipGetLastError();
+}
+
+}  // namespace mtpd
+
+namespace mtpd {
+
+hipError_t launch_allreduce_norm_quant(const PartialPtrs& parts, const uint16_t* residual, const float* gamma,
+                                       float eps, int64_t M, int64_t H, uint16_t* out_hidden, uint8_t* codes,
+                                       float* scales, hipStream_t stream)
+{
+    if (parts.n < 1 || parts.n > kMaxPartials) return hipErrorInvalidValue;
+    const int nstep = (int)((H + 2047) / 2048);
+    const int pmax = parts.n <= 2 ? 2 : parts.n <= 4 ? 4 : parts.n <= 8 ? 8 : 16;
+    const dim3 grid((unsigned)M), block(256);
+#define MTPD_AR_CASE(N, Q)                                                                                \
+    if (nstep == N && pmax == Q) {                                                                        \
+        hipLaunchKernelGGL((allreduce_norm_quant_kernel<N, Q>), grid, block, 0, stream, parts, residual,   \
+                           gamma, eps, (int)H, out_hidden, codes, scales);                                \
+        return hipGetLastError();                                                                         \
+    }
+#define MTPD_AR_STEPS(Q) \
+    MTPD_AR_CASE(1, Q) MTPD_AR_CASE(2, Q) MTPD_AR_CASE(3, Q) MTPD_AR_CASE(4, Q) \
+    MTPD_AR_CASE(5, Q) MTPD_AR_CASE(6, Q) MTPD_AR_CASE(7, Q) MTPD_AR_CASE(8, Q)
+    MTPD_AR_STEPS(2)
+    MTPD_AR_STEPS(4)
+    MTPD_AR_STEPS(8)
+    MTPD_AR_STEPS(16)
+#undef MTPD_AR_STEPS
+#undef MTPD_AR_CASE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace mtpd

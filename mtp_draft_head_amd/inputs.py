@@ -28,6 +28,10 @@ residual and in every row) are scaled x20 before rounding.  Norm weight
 U(0.5, 1.5) fp32; eps = 1e-6.  Weight N(0, 0.02) fp32, packed per 128x128
 block.
 
+Row-parallel partials (the inputs of the all-reduce folded into the norm):
+P arrays [M, H], each N(0, 1/P) in fp32 with the workload's outlier channels
+x20, rounded to bf16, so their sum has the spread of the hidden draw.
+
 Seeding: numpy PCG64 from SeedSequence(entropy=0x4D545044, spawn_key=...).
 Activations use spawn_key (workload_id, stream) with one stream per array.
 The weight uses spawn_key (100, H, V_full, block) with one stream per 128-row
@@ -275,6 +279,35 @@ def make(name_or_id):
         w_scales=scales,
         meta=meta,
     )
+
+
+def partials(name_or_id, P: int) -> np.ndarray:
+    """P row-parallel partial outputs for a workload: uint16 [P, M, H] bf16 bits.
+
+    Partial p is drawn from its own stream (spawn_key (workload_id, 10, P, p)).
+    """
+    w = get(name_or_id)
+    _, _, _, outl = _activations(w) if w.outliers else (None, None, None, np.zeros((0,), np.int64))
+    return _partials(lambda p: _rng(w.wid, 10, P, p), P, w.M, w.H, outl)
+
+
+def random_partials(seed: int, P: int, M: int, H: int, outliers: bool = False) -> np.ndarray:
+    """P partials of arbitrary shape for edge-case tests: uint16 [P, M, H]."""
+    outl = np.zeros((0,), np.int64)
+    if outliers and H >= 100:
+        outl = _rng(201, seed, M, H).choice(H, size=max(1, H // 100), replace=False)
+    return _partials(lambda p: _rng(202, seed, P, M, H, p), P, M, H, outl)
+
+
+def _partials(rng_for, P, M, H, outl):
+    out = np.empty((P, M, H), np.uint16)
+    sd = np.float32(1.0 / np.sqrt(P))
+    for p in range(P):
+        x = rng_for(p).standard_normal((M, H), dtype=np.float32) * sd
+        if len(outl):
+            x[:, outl] *= np.float32(20.0)
+        out[p] = to_bf16_bits(x)
+    return out
 
 
 def random_case(seed: int, M: int, H: int, V: int, outliers: bool = False, zero_rows=()):

@@ -9,6 +9,11 @@ the sharded argmax combine, which is plain Python over the C results.
 Function map (method steps as described on the pages):
   norm_quant      residual add, RMSNorm, bf16 recycled hidden + packed FP8
                   ("[Quant][MTP] Reuse packed FP8 logits inputs", Purpose)
+  allreduce_norm_quant
+                  the same step with the MTP layer's trailing all-reduce in
+                  front: norm input = sum of P partials + residual ("[Spec
+                  Decode][Perf] Fuse the MTP trailing all-reduce; local-argmax
+                  draft tokens", Summary)
   block_quant     the packing step alone (amax/448 scale per 128 columns)
   logits          block-scaled FP8 LM head on the packed activation
                   (same page, Purpose and Dependencies)
@@ -59,6 +64,8 @@ def _load():
     lib.ora_block_quant.argtypes = [P, I64, I64, P, P]
     lib.ora_norm_quant.restype = None
     lib.ora_norm_quant.argtypes = [P, P, P, ctypes.c_float, I64, I64, P, P, P, P, P]
+    lib.ora_allreduce_norm_quant.restype = None
+    lib.ora_allreduce_norm_quant.argtypes = [P, I64, P, P, ctypes.c_float, I64, I64, P, P, P, P, P]
     lib.ora_logits.restype = None
     lib.ora_logits.argtypes = [P, P, I64, P, I64, P, P, I64, P]
     lib.ora_argmax.restype = None
@@ -142,6 +149,31 @@ def norm_quant(hidden, residual, norm_weight, eps: float):
     rstd = np.empty((M,), np.float64)
     lib.ora_norm_quant(_ptr(h), _ptr(r), _ptr(g), ctypes.c_float(eps), M, H,
                        _ptr(out_h), _ptr(codes), _ptr(scales), _ptr(y), _ptr(rstd))
+    return dict(hidden=out_h, codes=codes, scales=scales, y=y, rstd=rstd)
+
+
+def allreduce_norm_quant(partials, residual, norm_weight, eps: float):
+    """norm_quant with norm input sum(partials) + residual, summed in fp64.
+
+    partials: uint16 [P, M, H] bf16 bit patterns; residual uint16 [M, H];
+    norm_weight float32 [H].  Returns norm_quant's dict.
+    """
+    lib = _load()
+    pp = _c(partials, np.uint16)
+    r = _c(residual, np.uint16)
+    g = _c(norm_weight, np.float32)
+    if pp.ndim != 3 or pp.shape[0] < 1:
+        raise ValueError("partials must be [P, M, H] with P >= 1")
+    P, M, H = pp.shape
+    if r.shape != (M, H) or g.shape != (H,) or H % BLOCK:
+        raise ValueError("shape mismatch")
+    out_h = np.empty((M, H), np.uint16)
+    codes = np.empty((M, H), np.uint8)
+    scales = np.empty((M, H // BLOCK), np.float32)
+    y = np.empty((M, H), np.float64)
+    rstd = np.empty((M,), np.float64)
+    lib.ora_allreduce_norm_quant(_ptr(pp), P, _ptr(r), _ptr(g), ctypes.c_float(eps), M, H,
+                                 _ptr(out_h), _ptr(codes), _ptr(scales), _ptr(y), _ptr(rstd))
     return dict(hidden=out_h, codes=codes, scales=scales, y=y, rstd=rstd)
 
 

@@ -10,8 +10,10 @@
  *   - residual add, then RMSNorm: the MTP layer's final all-reduce and
  *     RMSNorm ("[Quant][MTP] Reuse packed FP8 logits inputs", Purpose;
  *     "[Spec Decode][Perf] Fuse the MTP trailing all-reduce; local-argmax
- *     draft tokens", Summary).  On one GPU the all-reduce of a single
- *     partial is the identity, so the norm input is hidden + residual.
+ *     draft tokens", Summary).  ora_norm_quant takes the norm input as
+ *     hidden + residual (the all-reduce of a single partial is the
+ *     identity); ora_allreduce_norm_quant sums P row-parallel partials
+ *     first, standing in for the all-reduce on one GPU.
  *   - two outputs of the norm: the bf16 hidden recycled to the next MTP
  *     position and a packed FP8 activation for the shared LM head
  *     ("Reuse packed FP8 logits inputs", Purpose).  Packing is OCP E4M3FN
@@ -216,6 +218,31 @@ void ora_block_quant(const double *y, int64_t M, int64_t H, uint8_t *codes, floa
 /* ------------------------------------------------------------------------ */
 
 /*
+ * The norm and the two outputs for one row, from its norm input s[0..H) in
+ * fp64 (overwritten with y).  Returns rstd.
+ */
+static double ora_norm_row(double *s, const float *norm_weight, float eps, int64_t H,
+                           uint16_t *out_hidden, uint8_t *codes, float *scales, double *y_out)
+{
+    double ms = 0.0, rstd;
+    int64_t j;
+
+    for (j = 0; j < H; ++j)
+        ms += s[j] * s[j];
+    ms = ms / (double)H;
+    rstd = 1.0 / sqrt(ms + (double)eps);
+
+    for (j = 0; j < H; ++j) {
+        s[j] = s[j] * rstd * (double)norm_weight[j];
+        out_hidden[j] = ora_bf16_encode(s[j]);
+        if (y_out)
+            y_out[j] = s[j];
+    }
+    ora_block_quant_row(s, H, codes, scales);
+    return rstd;
+}
+
+/*
  * hidden, residual: [M][H] bfloat16 bit patterns, row-major.
  * norm_weight: [H] fp32.  eps: fp32, added to the mean square.
  * Outputs:
@@ -241,28 +268,55 @@ void ora_norm_quant(const uint16_t *hidden, const uint16_t *residual,
 
 #pragma omp parallel for schedule(dynamic, 1)
     for (m = 0; m < M; ++m) {
-        double *y = (double *)malloc((size_t)H * sizeof(double));
-        double ms = 0.0, rstd;
+        double *s = (double *)malloc((size_t)H * sizeof(double));
+        double rstd;
         int64_t j;
 
-        for (j = 0; j < H; ++j) {
-            double s = ora_bf16_decode(hidden[m * H + j]) + ora_bf16_decode(residual[m * H + j]);
-            y[j] = s;
-            ms += s * s;
-        }
-        ms = ms / (double)H;
-        rstd = 1.0 / sqrt(ms + (double)eps);
+        for (j = 0; j < H; ++j)
+            s[j] = ora_bf16_decode(hidden[m * H + j]) + ora_bf16_decode(residual[m * H + j]);
+        rstd = ora_norm_row(s, norm_weight, eps, H, out_hidden + m * H, codes + m * H, scales + m * KB,
+                            y_out ? y_out + m * H : NULL);
         if (rstd_out)
             rstd_out[m] = rstd;
+        free(s);
+    }
+}
+
+/*
+ * The same step with the MTP layer's trailing all-reduce in front of the
+ * norm ("[Spec Decode][Perf] Fuse the MTP trailing all-reduce; local-argmax
+ * draft tokens", Summary): the norm input is the sum of the P row-parallel
+ * partial outputs plus the residual,
+ *   s = sum_p partials[p] + residual
+ * taken in fp64 (exact for bf16 inputs whose exponents span less than about
+ * 40 binades), then normalized and packed exactly as ora_norm_quant does.
+ * partials: [P][M][H] bf16, contiguous.
+ */
+void ora_allreduce_norm_quant(const uint16_t *partials, int64_t P, const uint16_t *residual,
+                              const float *norm_weight, float eps, int64_t M, int64_t H,
+                              uint16_t *out_hidden, uint8_t *codes, float *scales,
+                              double *y_out, double *rstd_out)
+{
+    int64_t KB = H / ORA_BLOCK;
+    int64_t m;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (m = 0; m < M; ++m) {
+        double *s = (double *)malloc((size_t)H * sizeof(double));
+        double rstd;
+        int64_t j, p;
 
         for (j = 0; j < H; ++j) {
-            y[j] = y[j] * rstd * (double)norm_weight[j];
-            out_hidden[m * H + j] = ora_bf16_encode(y[j]);
-            if (y_out)
-                y_out[m * H + j] = y[j];
+            double acc = 0.0;
+            for (p = 0; p < P; ++p)
+                acc += ora_bf16_decode(partials[(p * M + m) * H + j]);
+            s[j] = acc + ora_bf16_decode(residual[m * H + j]);
         }
-        ora_block_quant_row(y, H, codes + m * H, scales + m * KB);
-        free(y);
+        rstd = ora_norm_row(s, norm_weight, eps, H, out_hidden + m * H, codes + m * H, scales + m * KB,
+                            y_out ? y_out + m * H : NULL);
+        if (rstd_out)
+            rstd_out[m] = rstd;
+        free(s);
     }
 }
 

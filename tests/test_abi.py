@@ -35,7 +35,8 @@ def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"mtpd_norm_quant", "mtpd_fp8_lmhead_argmax", "mtpd_draft_tail", "mtpd_workspace_bytes",
             "mtpd_status_name", "mtpd_last_error", "mtpd_clear_error", "mtpd_abi_version",
-            "mtpd_lmhead_plan", "mtpd_draft_tail_plan"} <= set(names)
+            "mtpd_lmhead_plan", "mtpd_draft_tail_plan", "mtpd_allreduce_norm_quant",
+            "mtpd_argmax_combine"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -45,7 +46,7 @@ def test_status_names_and_version(L):
         "MTPD_OK", "MTPD_ERR_NULL", "MTPD_ERR_SHAPE", "MTPD_ERR_ALIGN", "MTPD_ERR_ALIAS",
         "MTPD_ERR_WORKSPACE", "MTPD_ERR_HIP"]
     assert L.mtpd_status_name(99).decode() == "MTPD_UNKNOWN"
-    assert L.mtpd_abi_version() == 2
+    assert L.mtpd_abi_version() == 3
 
 
 def test_workspace_bytes(L):
@@ -149,6 +150,47 @@ def test_draft_tail_validation(L):
     assert dt(ws_bytes=8) == WORKSPACE
     assert dt(out_max=A + 0x7000000) == ALIAS
     assert dt(M=0) == OK
+
+
+def test_allreduce_norm_quant_validation(L):
+    def ar(ptrs=(A, A + 0x400000), n=None, residual=A + 0x1000000, M=4, H=256, out_h=A + 0x3000000,
+           codes=A + 0x4000000):
+        n = len(ptrs) if n is None else n
+        arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs) if ptrs is not None else None
+        qa = QAct(codes, A + 0x5000000, M, H)
+        L.mtpd_clear_error()
+        return L.mtpd_allreduce_norm_quant(arr, n, residual, A + 0x2000000, 1e-6,
+                                           M, H, out_h, ctypes.byref(qa), None)
+    assert ar(n=0) == SHAPE
+    assert ar(n=17, ptrs=[A + i * 0x10000 for i in range(17)]) == SHAPE
+    assert ar(ptrs=None, n=2) == NULL
+    assert ar(ptrs=(A, None)) == NULL
+    assert ar(ptrs=(A, A + 0x400000 + 8)) == ALIGN
+    assert ar(H=200) == SHAPE
+    assert ar(residual=None) == NULL
+    assert ar(out_h=A + 0x400000) == ALIAS                # output over the second partial
+    assert ar(codes=A + 0x400000 + 256) == ALIAS
+    assert ar(M=0) == OK
+
+
+def test_argmax_combine_validation(L):
+    def cb(offs=(0, 1024), n=None, rows=4, lmax=A, lidx=A + 0x1000, omax=A + 0x2000, oidx=A + 0x3000):
+        n = len(offs) if n is None else n
+        arr = (ctypes.c_int64 * max(1, len(offs)))(*offs) if offs is not None else None
+        L.mtpd_clear_error()
+        return L.mtpd_argmax_combine(lmax, lidx, arr, n, rows, omax, oidx, None)
+    assert cb(n=0) == SHAPE
+    assert cb(offs=list(range(65))) == SHAPE
+    assert cb(offs=(0, -128)) == SHAPE
+    assert cb(offs=(0, 1 << 31)) == SHAPE
+    assert cb(offs=None, n=2) == NULL
+    assert cb(rows=-1) == SHAPE
+    assert cb(rows=(1 << 24) + 1) == SHAPE
+    assert cb(lmax=None) == NULL
+    assert cb(oidx=A + 0x3002) == ALIGN
+    assert cb(omax=A + 8) == ALIAS                        # output inside local_max ([2][4] f32)
+    assert cb(oidx=A + 0x2008) == ALIAS                   # the two outputs overlap
+    assert cb(rows=0, lmax=None, lidx=None, omax=None, oidx=None) == OK
 
 
 def test_binding_refuses_cpu_tensors():

@@ -188,3 +188,76 @@ def test_workload_norm_quant_invariants(name, workloads):
     _quant_invariants(out["y"], out["codes"], out["scales"])
     c2, s2 = oracle.block_quant(dequant_f64(out["codes"], out["scales"]))
     assert np.array_equal(c2, out["codes"]) and np.array_equal(s2, out["scales"])
+
+
+# --------------------------------------------------------------------------
+# the all-reduce folded into the norm: norm input = sum of P partials + residual
+# ("[Spec Decode][Perf] Fuse the MTP trailing all-reduce; local-argmax draft
+# tokens", Summary).  Pinned by reduction to the norm_quant oracle (itself
+# pinned above) on partial sets whose sum is known exactly.
+# --------------------------------------------------------------------------
+
+def _same(a, b):
+    for k in ("hidden", "codes", "scales", "y", "rstd"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_allreduce_single_partial_is_norm_quant():
+    rng = np.random.default_rng(11)
+    h = bf16_bits(rng.standard_normal((3, 384)))
+    r = bf16_bits(rng.standard_normal((3, 384)))
+    g = rng.uniform(0.5, 1.5, 384).astype(np.float32)
+    _same(oracle.allreduce_norm_quant(h[None], r, g, EPS), run(h, r, g))
+
+
+@pytest.mark.parametrize("P,k", [(2, 1), (3, 0), (3, 2), (8, 5)])
+def test_allreduce_one_nonzero_partial_at_any_position(P, k):
+    """Zero partials contribute nothing, wherever the live one sits (catches a
+    wrong partial/row stride: every row differs)."""
+    rng = np.random.default_rng(12 + P + k)
+    M, H = 4, 256
+    h = bf16_bits(rng.standard_normal((M, H)) * rng.uniform(0.1, 10, (M, 1)))
+    r = bf16_bits(rng.standard_normal((M, H)))
+    g = rng.uniform(0.5, 1.5, H).astype(np.float32)
+    parts = np.zeros((P, M, H), np.uint16)
+    parts[k] = h
+    _same(oracle.allreduce_norm_quant(parts, r, g, EPS), run(h, r, g))
+
+
+@pytest.mark.parametrize("P", [2, 4, 8])
+def test_allreduce_exact_split_sums_back(P):
+    """Partials h/P (exact: a power-of-two scaling of bf16 values) sum to h, so
+    the result is norm_quant(h, r); a dropped or doubled partial is off by h/P."""
+    rng = np.random.default_rng(20 + P)
+    M, H = 5, 512
+    h = bf16_bits(rng.standard_normal((M, H)))
+    r = bf16_bits(rng.standard_normal((M, H)))
+    g = rng.uniform(0.5, 1.5, H).astype(np.float32)
+    part = bf16_bits(bf16_vals(h) / P)
+    assert np.array_equal(bf16_vals(part) * P, bf16_vals(h))
+    _same(oracle.allreduce_norm_quant(np.stack([part] * P), r, g, EPS), run(h, r, g))
+
+
+def test_allreduce_cancelling_partials_with_distinct_rows():
+    """p0 = h, p1 = x, p2 = -x (negation is exact): the sum is h whatever x is;
+    x differs in every row and partial, so any mixing of partials or rows shows."""
+    rng = np.random.default_rng(31)
+    M, H = 6, 384
+    h = bf16_bits(rng.standard_normal((M, H)))
+    x = bf16_bits(rng.standard_normal((M, H)) * 3.0)
+    r = bf16_bits(rng.standard_normal((M, H)))
+    g = rng.uniform(0.5, 1.5, H).astype(np.float32)
+    _same(oracle.allreduce_norm_quant(np.stack([h, x, x ^ np.uint16(0x8000)]), r, g, EPS), run(h, r, g))
+    # the order of the partials does not matter (the sum is exact in fp64)
+    _same(oracle.allreduce_norm_quant(np.stack([x ^ np.uint16(0x8000), h, x]), r, g, EPS), run(h, r, g))
+
+
+def test_allreduce_constant_partials_closed_form():
+    """Constant partials c_p and zero residual: y = S / sqrt(S^2 + eps) with S = sum c_p."""
+    H = 256
+    cs = [0.5, -0.25, 3.0, 1.125]
+    parts = np.stack([bf16_bits(np.full((1, H), c)) for c in cs])
+    S = float(sum(cs))
+    out = oracle.allreduce_norm_quant(parts, bf16_bits(np.zeros((1, H))), np.ones(H, np.float32), EPS)
+    assert np.allclose(out["y"], S / np.sqrt(S * S + np.float64(np.float32(EPS))), rtol=1e-15, atol=0)
+    assert np.all((out["codes"] & 0x7F) == 0x7E)
