@@ -15,7 +15,8 @@
 //    K group l / 16) would instead issue one request per lane, which caps
 //    a CU well below its share of HBM bandwidth.  Inside a row's 128-byte
 //    slot chunk c sits at position c ^ s(r); s makes the fragment reads
-//    conflict-free (see ring_pos).
+//    conflict-free (see ring_pos).  The weight copies are non-temporal
+//    (read once per launch); measured 4-10% faster than default caching.
 //  - The activation rows of a block (at most 8 * MA of them) travel in the
 //    same ring slot the same way, so the loop has no vector-memory load into
 //    registers at all: a register load would make the compiler drain the
@@ -80,6 +81,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(
 #pragma clang diagnostic ignored "-Winline-asm"   // M0 is reserved; the kernel uses it for nothing else
 __device__ __forceinline__ void lds_copy16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+// The same for the weight stream, marked non-temporal: each weight byte is
+// read once per launch, so its lines should not push the activation blocks
+// and scale tables (re-read by every workgroup) out of the caches.
+__device__ __forceinline__ void lds_copy16_stream(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                  :
                  : "v"(voff), "s"(sbase), "s"(lds)
                  : "memory", "m0");
@@ -165,7 +175,7 @@ __global__ __launch_bounds__(64) void lmhead_stream_kernel(
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int q = 0; q < 2; ++q) lds_copy16(wb, woff[nt][q], ring0 + (uint32_t)(j * SLOT + (nt * 2 + q) * 64) * 16u);
+            for (int q = 0; q < 2; ++q) lds_copy16_stream(wb, woff[nt][q], ring0 + (uint32_t)(j * SLOT + (nt * 2 + q) * 64) * 16u);
 #pragma unroll
         for (int q = 0; q < MA; ++q) lds_copy16(ab, aoff[q], ring0 + (uint32_t)(j * SLOT + (NT * 2 + q) * 64) * 16u);
     };
@@ -378,7 +388,7 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int q = 0; q < 2; ++q) lds_copy16(wb, woff[nt][q], wring0 + (uint32_t)(j * WSLOT + (nt * 2 + q) * 64) * 16u);
+            for (int q = 0; q < 2; ++q) lds_copy16_stream(wb, woff[nt][q], wring0 + (uint32_t)(j * WSLOT + (nt * 2 + q) * 64) * 16u);
 #pragma unroll
         for (int i2 = 0; i2 < APW; ++i2)
             lds_copy16(ab, aoff[i2], aring0 + (uint32_t)(j * ASLOT + (wave + NW * i2) * 64) * 16u);
@@ -610,7 +620,7 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
     auto refill = [&](int j, int kb) {
         const uint8_t* wb = wbase + (size_t)kb * kBlock;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) lds_copy16(wb, woff[q], ring0 + (uint32_t)(j * SLOT + q * 64) * 16u);
+        for (int q = 0; q < 2; ++q) lds_copy16_stream(wb, woff[q], ring0 + (uint32_t)(j * SLOT + q * 64) * 16u);
     };
 
     // 1. per wave: the weight-scale row and the first D blocks of its range

@@ -215,12 +215,13 @@ def test_stream_kernel_shapes(M, shape, monkeypatch):
     assert torch.equal(i0, i1)
 
 
-@pytest.mark.parametrize("shape", ["2,4,4", "1,8,4", "2,4,3", "1,4,4", "1,4,3", "1,4,6"])
+@pytest.mark.parametrize("shape", ["2,4,3", "2,4,4", "2,4,5", "1,8,4", "1,4,3", "1,4,4", "1,4,6", "2,4,6"])
 @pytest.mark.parametrize("M", [17, 32, 33, 64])
 def test_stream_rows_kernel_shapes(M, shape, monkeypatch):
     """17..64 rows: every compiled shape of the streaming kernel with a shared
     activation ring (tiles per wave, waves, ring depth; K = 9 blocks) meets the
-    oracle and picks the decode kernel's indices."""
+    oracle and picks the decode kernel's indices.  (Shapes not compiled for
+    the row count fall back to the default shape.)"""
     d = inputs.random_case(29 + M, M, 1152, 4096, outliers=True)
     h, r, g, wc, ws = to_dev(d)
     monkeypatch.setenv("MTPD_LMHEAD_KERNEL", "decode")
@@ -234,6 +235,22 @@ def test_stream_rows_kernel_shapes(M, shape, monkeypatch):
     torch.cuda.synchronize()
     check_lmhead(codes, scales, d, m1, i1)
     assert torch.equal(i0, i1)
+
+
+def test_stream_rows_kernel_vocab_shard_shape(workloads):
+    """64 rows on one GPU's 18944-row vocab shard (the decode c=64 weight's
+    first 148 blocks): every row against the oracle."""
+    d = workloads("decode_c64_full")
+    h, r, g, wc, ws = to_dev(d)
+    S = 18944
+    say(f"  plan: {mtpd.lmhead_plan(64, S, 6144)}")
+    _, codes, scales, _, _ = mtpd.draft_tail(h, r, g, d["eps"], wc, ws)
+    m, i = mtpd.fp8_lmhead_argmax(codes, scales, wc[:S], ws[:S // 128])
+    c, s = host(codes), host(scales)
+    ref = oracle.argmax(c, s, d["w_codes"][:S], d["w_scales"][:S // 128])
+    say("  " + str(parity.check_argmax(host(m), host(i), ref,
+                                        logit_row=lambda k: oracle.logits(c, s, d["w_codes"][:S],
+                                                                          d["w_scales"][:S // 128], rows=[k])[0])))
 
 
 @pytest.mark.parametrize("H,V", [(128, 256), (1152, 2048), (2304, 4096), (6144, 18944)])
