@@ -26,6 +26,12 @@ steps next to it under tensor parallelism, on one GPU's share:
                  (standing in for the peers' outputs) + the LM head;
                  roofline on the all-reduce + norm kernel (the partial sets
                  are rotated past the Infinity Cache too)
+  chain          5 successive MTP positions per step, each a draft_tail call
+                 whose hidden input is the previous position's recycled bf16
+                 hidden (an identity stand-in for the layer body, which needs
+                 real weights; the residual is kept); the step is one graph
+                 segment of 5 dependent tails, and the line reports the time
+                 per position against a lone tail
 
 Prints ONE JSON line.  --gpus above 1 is refused: this build drives one GPU.
 """
@@ -100,6 +106,7 @@ def dominant_kernel(M, H, V):
 
 N_SHARDS = 8      # vocab shards of the vocab_shards variant
 N_PARTIALS = 8    # row-parallel partials of the allreduce_tail variant
+N_CHAIN = 5       # MTP positions per step of the chain variant
 
 
 def allreduce_norm_bytes(P, M, H) -> int:
@@ -118,6 +125,8 @@ def roofline_kernel(variant, M, H, V):
         Vs = V // N_SHARDS
         plan = mtpd.lmhead_plan(M, Vs, H)
         return plan.split("<")[0].split()[0], "lmhead", lmhead_bytes(M, H, Vs), plan, 2.0 * M * H * Vs
+    if variant == "chain":
+        variant = "tail"
     if variant == "allreduce_tail":
         name = "allreduce_norm_quant_kernel"
         return name, "norm", allreduce_norm_bytes(N_PARTIALS, M, H), f"{name} grid={M}x256 P={N_PARTIALS}", 0.0
@@ -232,7 +241,7 @@ def cpu_baseline(d, seconds: float, variant: str = "tail", parts=None):
     t1 = run(1)
     n = max(1, min(4096, int(seconds / max(t1, 1e-4))))
     t = run(n)
-    what = {"tail": "full tail", "vocab_shards": f"full tail with {N_SHARDS} vocab shards combined",
+    what = {"tail": "full tail", "chain": "full tail (one MTP position)", "vocab_shards": f"full tail with {N_SHARDS} vocab shards combined",
             "allreduce_tail": f"full tail with the {N_PARTIALS}-partial sum"}[variant]
     return {"value": n / t, "unit": "rows/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{n} rows of {w.name} (M={w.M} H={H} V={V}, rows taken cyclically), {what} "
@@ -245,7 +254,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_c1_tp8_shard")
-    ap.add_argument("--variant", default="tail", choices=["tail", "vocab_shards", "allreduce_tail"])
+    ap.add_argument("--variant", default="tail", choices=["tail", "vocab_shards", "allreduce_tail", "chain"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -300,7 +309,19 @@ def main() -> int:
     extra = {}
 
     parts_np = None
-    if variant == "tail":
+    if variant == "chain":
+        chain_out = [tuple(torch.empty_like(x) for x in out) for _ in range(N_CHAIN - 1)] + [out]
+
+        def step(i):
+            hin = hid
+            for p in range(N_CHAIN):
+                mtpd.draft_tail(hin, res, g, d["eps"], wcs[(i * N_CHAIN + p) % n_copies],
+                                wss[(i * N_CHAIN + p) % n_copies], workspace=wsp, out=chain_out[p])
+                hin = chain_out[p][0]
+
+        def kernel_step(i):
+            mtpd.draft_tail(hid, res, g, d["eps"], wcs[i % n_copies], wss[i % n_copies], workspace=wsp, out=out)
+    elif variant == "tail":
         def step(i):
             mtpd.draft_tail(hid, res, g, d["eps"], wcs[i % n_copies], wss[i % n_copies], workspace=wsp, out=out)
 
@@ -396,6 +417,12 @@ def main() -> int:
 
     log(f"[bench] timing {K} steps (one HIP graph)")
     ms_step, g1 = timed_graph(step)
+    # sanity: the timed outputs are the real ones
+    torch.cuda.synchronize()
+    ref_idx = out[4].clone()
+    step(0)
+    torch.cuda.synchronize()
+    assert torch.equal(ref_idx, out[4]), "graph replay and eager call disagree"
     log(f"[bench] timing {K} launches of the roofline kernel (one HIP graph)")
     ms_kernel, g2 = timed_graph(kernel_step)
     del g1, g2
@@ -407,21 +434,20 @@ def main() -> int:
         ms_lm_alone, g3 = timed_graph(lm_alone)
         del g3
 
-    # sanity: the timed outputs are the real ones
-    torch.cuda.synchronize()
-    ref_idx = out[4].clone()
-    step(0)
-    torch.cuda.synchronize()
-    assert torch.equal(ref_idx, out[4]), "graph replay and eager call disagree"
-
     flops = 2.0 * M * H * V
     # the roofline kernel's time: the fused tail is the whole step (one launch
     # per step); otherwise the kernel timed alone
-    k_us = ms_step * 1e3 if kind == "tail" else ms_kernel * 1e3
+    if variant == "chain":
+        k_us = ms_kernel * 1e3 if kind == "tail" else None
+    else:
+        k_us = ms_step * 1e3 if kind == "tail" else ms_kernel * 1e3
+    if k_us is None:
+        raise SystemExit("the chain variant is defined for the one-row fused tail (decode_c1_tp8_shard)")
     gbps = alg / (k_us * 1e-6) / 1e9
     tflops = kflops / (k_us * 1e-6) / 1e12
     compute_bound = kflops / alg > (FP8_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBPS * 1e9)
-    traffic = traffic_from_profile(kname, w.name, variant)
+    # the chain's roofline kernel is the lone tail's: same launch, same traffic summary
+    traffic = traffic_from_profile(kname, w.name, "tail" if variant == "chain" else variant)
     if compute_bound:
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tflops / FP8_PEAK_TFLOPS, 4), "traffic": traffic}
@@ -434,6 +460,11 @@ def main() -> int:
     # the full-vocab LM head alone (the tail's second launch), for reference
     if variant == "tail":
         lm_us = ms_kernel * 1e3
+    elif variant == "chain":
+        lm_us = None
+        extra["positions_per_step"] = N_CHAIN
+        extra["us_per_position_chained"] = round(ms_step * 1e3 / N_CHAIN, 3)
+        extra["us_lone_tail"] = round(ms_kernel * 1e3, 3)
     elif variant == "allreduce_tail":
         lm_us = ms_lm_alone * 1e3
     else:
@@ -449,11 +480,12 @@ def main() -> int:
               "weight_copies_rotated": n_copies, "timing": "K steps in one HIP graph"}
     if variant != "tail":
         config["variant"] = variant
-        config["shards" if variant == "vocab_shards" else "partials"] = (
-            N_SHARDS if variant == "vocab_shards" else N_PARTIALS)
+        config.update({"vocab_shards": {"shards": N_SHARDS}, "allreduce_tail": {"partials": N_PARTIALS},
+                       "chain": {"positions": N_CHAIN}}[variant])
+    rows_per_step = M * (N_CHAIN if variant == "chain" else 1)
     rec = {
         "metric": METRIC,
-        "value": round(M / (ms_step * 1e-3), 1),
+        "value": round(rows_per_step / (ms_step * 1e-3), 1),
         "unit": "rows/s",
         "n_gpus": 1,
         "steps": K,
@@ -466,7 +498,7 @@ def main() -> int:
         "data": "synthetic",
         "config": config,
     }
-    if variant == "tail":
+    if variant in ("tail", "chain"):
         rec["draft_tail_plan"] = tail_plan
     if lm_us is not None:
         rec["lmhead"] = {"kernel": plan, "us": round(lm_us, 3), "GB/s": round(lm_alg / (lm_us * 1e-6) / 1e9, 1),
