@@ -20,6 +20,9 @@ Function map (method steps as described on the pages):
   argmax          greedy local argmax, lowest index on equal maxima
                   ("[Spec Decode][Perf] Fuse the MTP trailing all-reduce;
                   local-argmax draft tokens", Summary)
+  topk            the k largest fp32 logits per row, descending, lowest index
+                  first among equal values ("feat(glm52): add checkpoint-native
+                  MTP speculative decoding", Accuracy: top-8 / top-32 overlap)
   argmax_sharded  the vocab-parallel view: per-shard local argmaxes combined
                   by (max desc, global index asc) (same page, Summary and
                   Accuracy)
@@ -70,6 +73,8 @@ def _load():
     lib.ora_logits.argtypes = [P, P, I64, P, I64, P, P, I64, P]
     lib.ora_argmax.restype = None
     lib.ora_argmax.argtypes = [P, P, I64, P, I64, P, P, I64, P, P, P, P]
+    lib.ora_topk.restype = None
+    lib.ora_topk.argtypes = [P, P, I64, P, I64, P, P, I64, I64, P, P]
     lib.ora_num_threads.restype = ctypes.c_int
     lib.ora_num_threads.argtypes = []
     _lib = lib
@@ -235,6 +240,20 @@ def argmax(codes, scales, w_codes, w_scales, rows=None):
         lib.ora_argmax(_ptr(a), _ptr(sa), H, _ptr(rr), n, _ptr(wq), _ptr(ws), V,
                        _ptr(out_max), _ptr(out_idx), _ptr(z1), _ptr(z2))
     return dict(max=out_max, idx=out_idx, z1=z1, z2=z2)
+
+
+def topk(codes, scales, w_codes, w_scales, k: int, rows=None):
+    """Top-k per row: (values float32 [n, k], indices int32 [n, k]), descending."""
+    lib = _load()
+    a, sa, wq, ws, A, H, V = _check_lmhead(codes, scales, w_codes, w_scales)
+    rr, n = _rows_arg(rows, A)
+    if not 1 <= k <= V:
+        raise ValueError("k must lie in [1, V]")
+    vals = np.empty((n, k), np.float32)
+    idx = np.empty((n, k), np.int32)
+    if n:
+        lib.ora_topk(_ptr(a), _ptr(sa), H, _ptr(rr), n, _ptr(wq), _ptr(ws), V, int(k), _ptr(vals), _ptr(idx))
+    return vals, idx
 
 
 def combine_shards(local_max, local_idx, offsets):

@@ -418,6 +418,52 @@ void ora_argmax(const uint8_t *act_codes, const float *act_scales, int64_t H,
     free(z);
 }
 
+/*
+ * Greedy local top-k: the k vocab rows with the largest fp32 logits, in
+ * descending order of the fp32 logit, equal logits in ascending index order
+ * (+0 and -0 equal), the same decision rule as ora_argmax (k == 1 gives its
+ * result).  The pages compare draft and reference distributions by their
+ * top-8 and top-32 sets ("feat(glm52): add checkpoint-native MTP speculative
+ * decoding", Accuracy).  out_val, out_idx: [n_rows][k]; 1 <= k <= V.
+ * A plain selection: k passes over the row, each taking the best entry not
+ * yet taken.
+ */
+void ora_topk(const uint8_t *act_codes, const float *act_scales, int64_t H,
+              const int32_t *rows, int64_t n_rows,
+              const uint8_t *w_codes, const float *w_scales, int64_t V, int64_t k,
+              float *out_val, int32_t *out_idx)
+{
+    double *z = (double *)malloc((size_t)(n_rows * V) * sizeof(double));
+    int64_t i;
+
+    ora_logits(act_codes, act_scales, H, rows, n_rows, w_codes, w_scales, V, z);
+
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n_rows; ++i) {
+        const double *zr = z + i * V;
+        unsigned char *taken = (unsigned char *)calloc((size_t)V, 1);
+        int64_t e, v;
+        for (e = 0; e < k; ++e) {
+            int64_t best = -1;
+            float bestf = 0.0f;
+            for (v = 0; v < V; ++v) {
+                float f = (float)zr[v];
+                if (taken[v])
+                    continue;
+                if (best < 0 || f > bestf) {   /* strict: the lowest index wins equal values */
+                    best = v;
+                    bestf = f;
+                }
+            }
+            taken[best] = 1;
+            out_val[i * k + e] = bestf;
+            out_idx[i * k + e] = (int32_t)best;
+        }
+        free(taken);
+    }
+    free(z);
+}
+
 int ora_num_threads(void)
 {
 #ifdef _OPENMP

@@ -147,3 +147,56 @@ def test_mtp5_near_tie_rows_are_planted(workloads):
     assert len(rows) == 16
     assert np.all(gap > 1e-6) and np.all(gap < 1e-3)
     assert [int(x) for x in r["idx"]] == [p[1] for p in planted]
+
+
+# --------------------------------------------------------------------------
+# top-k ("feat(glm52): add checkpoint-native MTP speculative decoding",
+# Accuracy: the top-8 and top-32 sets of draft and reference are compared)
+# --------------------------------------------------------------------------
+
+def test_topk_of_one_is_the_argmax():
+    a, sa, w, sw = small_case(41, 6, 384, 640)
+    v, i = oracle.topk(a, sa, w, sw, 1)
+    ref = oracle.argmax(a, sa, w, sw)
+    assert np.array_equal(i[:, 0], ref["idx"]) and np.array_equal(v[:, 0], ref["max"])
+
+
+@pytest.mark.parametrize("k", [2, 8, 32])
+def test_topk_matches_a_stable_sort_of_fp32_logits(k):
+    """Against numpy's stable sort of the fp32 logits by descending value (a
+    library ordering of the oracle's own logits, which are pinned above)."""
+    a, sa, w, sw = small_case(42 + k, 5, 512, 1024)
+    v, i = oracle.topk(a, sa, w, sw, k)
+    z32 = oracle.logits(a, sa, w, sw).astype(np.float32)
+    for r in range(5):
+        order = np.argsort(-z32[r].astype(np.float64), kind="stable")[:k]
+        assert np.array_equal(i[r], order)
+        assert np.array_equal(v[r], z32[r][order])
+        assert np.all(np.diff(v[r].astype(np.float64)) <= 0)
+
+
+def test_topk_brute_force_on_python_tuples():
+    """Pure-Python sort of (-value, index) pairs on a tiny case."""
+    a, sa, w, sw = small_case(47, 2, 256, 256)
+    z32 = oracle.logits(a, sa, w, sw).astype(np.float32)
+    v, i = oracle.topk(a, sa, w, sw, 8)
+    for r in range(2):
+        pairs = sorted((-float(z32[r, c]), c) for c in range(256))[:8]
+        assert [c for _, c in pairs] == list(i[r])
+
+
+def test_topk_planted_ties_come_in_index_order():
+    d = inputs.make("tiny")
+    nq = oracle.norm_quant(d["hidden"], d["residual"], d["norm_weight"], d["eps"])
+    v, i = oracle.topk(nq["codes"], nq["scales"], d["w_codes"], d["w_scales"], 4)
+    for row, lo, hi in d["meta"]["ties"]:
+        assert i[row, 0] == lo and i[row, 1] == hi and v[row, 0] == v[row, 1]
+
+
+def test_topk_of_a_zero_row_is_the_lowest_indices():
+    """A zero activation row makes every logit 0: the top-k are indices 0..k-1."""
+    a, sa, w, sw = small_case(48, 3, 256, 384)
+    a = a.copy(); sa = sa.copy()
+    a[1] = 0; sa[1] = 0
+    v, i = oracle.topk(a, sa, w, sw, 8)
+    assert list(i[1]) == list(range(8)) and np.all(v[1] == 0)
