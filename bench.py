@@ -32,6 +32,10 @@ steps next to it under tensor parallelism, on one GPU's share:
                  real weights; the residual is kept); the step is one graph
                  segment of 5 dependent tails, and the line reports the time
                  per position against a lone tail
+  topk           norm_quant, then the LM head's top-k (--topk, default 8)
+                 instead of the argmax: the streaming kernel writes sorted
+                 per-(tile, wave) candidate lists and a merge launch selects;
+                 roofline on the streaming kernel
 
 Prints ONE JSON line.  --gpus above 1 is refused: this build drives one GPU.
 """
@@ -107,6 +111,12 @@ def dominant_kernel(M, H, V):
 N_SHARDS = 8      # vocab shards of the vocab_shards variant
 N_PARTIALS = 8    # row-parallel partials of the allreduce_tail variant
 N_CHAIN = 5       # MTP positions per step of the chain variant
+TOPK_K = 8        # k of the topk variant (--topk)
+
+
+def topk_list_bytes(M, V, k) -> int:
+    """Candidate-list bytes one top-k pass writes (and its merge reads once)."""
+    return M * (V // 32) * k * 8
 
 
 def allreduce_norm_bytes(P, M, H) -> int:
@@ -127,6 +137,12 @@ def roofline_kernel(variant, M, H, V):
         return plan.split("<")[0].split()[0], "lmhead", lmhead_bytes(M, H, Vs), plan, 2.0 * M * H * Vs
     if variant == "chain":
         variant = "tail"
+    if variant == "topk":
+        mt = 2 if M <= 32 else 4
+        name = "lmhead_stream_rows_kernel"
+        tiles = V // 128
+        return (name, "lmhead", lmhead_bytes(min(M, 64), H, V) + topk_list_bytes(min(M, 64), V, TOPK_K),
+                f"{name}<{mt},2,4,3,topk> grid={min(tiles, 256)}x256", 2.0 * min(M, 64) * H * V)
     if variant == "allreduce_tail":
         name = "allreduce_norm_quant_kernel"
         return name, "norm", allreduce_norm_bytes(N_PARTIALS, M, H), f"{name} grid={M}x256 P={N_PARTIALS}", 0.0
@@ -234,6 +250,8 @@ def cpu_baseline(d, seconds: float, variant: str = "tail", parts=None):
             nq = oracle.norm_quant(d["hidden"][rows], d["residual"][rows], d["norm_weight"], d["eps"])
         if variant == "vocab_shards":
             oracle.argmax_sharded(nq["codes"], nq["scales"], d["w_codes"], d["w_scales"], V // N_SHARDS)
+        elif variant == "topk":
+            oracle.topk(nq["codes"], nq["scales"], d["w_codes"], d["w_scales"], TOPK_K)
         else:
             oracle.argmax(nq["codes"], nq["scales"], d["w_codes"], d["w_scales"])
         return time.perf_counter() - t0
@@ -241,7 +259,8 @@ def cpu_baseline(d, seconds: float, variant: str = "tail", parts=None):
     t1 = run(1)
     n = max(1, min(4096, int(seconds / max(t1, 1e-4))))
     t = run(n)
-    what = {"tail": "full tail", "chain": "full tail (one MTP position)", "vocab_shards": f"full tail with {N_SHARDS} vocab shards combined",
+    what = {"tail": "full tail", "chain": "full tail (one MTP position)",
+            "topk": f"norm + pack + LM head + top-{TOPK_K}", "vocab_shards": f"full tail with {N_SHARDS} vocab shards combined",
             "allreduce_tail": f"full tail with the {N_PARTIALS}-partial sum"}[variant]
     return {"value": n / t, "unit": "rows/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{n} rows of {w.name} (M={w.M} H={H} V={V}, rows taken cyclically), {what} "
@@ -254,7 +273,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_c1_tp8_shard")
-    ap.add_argument("--variant", default="tail", choices=["tail", "vocab_shards", "allreduce_tail", "chain"])
+    ap.add_argument("--variant", default="tail", choices=["tail", "vocab_shards", "allreduce_tail", "chain", "topk"])
+    ap.add_argument("--topk", type=int, default=8, help="k of the topk variant (1..32)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -263,6 +283,8 @@ def main() -> int:
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a run with "
                          "--copy-calibration-mib into the traffic summary under profiles/")
     args = ap.parse_args()
+    global TOPK_K
+    TOPK_K = args.topk
     if args.summarize_pmc:
         return summarize_pmc(args.workload, *args.summarize_pmc, args.copy_calibration_mib, args.variant)
 
@@ -321,6 +343,20 @@ def main() -> int:
 
         def kernel_step(i):
             mtpd.draft_tail(hid, res, g, d["eps"], wcs[i % n_copies], wss[i % n_copies], workspace=wsp, out=out)
+    elif variant == "topk":
+        tk_out = (torch.empty((M, TOPK_K), dtype=torch.float32, device=dev),
+                  torch.empty((M, TOPK_K), dtype=torch.int32, device=dev))
+        tk_ws = mtpd.Workspace(dev)
+        tk_ws.get_bytes(mtpd.topk_workspace_bytes(M, V, TOPK_K))
+
+        def step(i):
+            mtpd.norm_quant(hid, res, g, d["eps"], out=out[:3])
+            mtpd.fp8_lmhead_topk(out[1], out[2], wcs[i % n_copies], wss[i % n_copies], TOPK_K, workspace=tk_ws,
+                                 out=tk_out)
+
+        def kernel_step(i):
+            mtpd.fp8_lmhead_topk(out[1], out[2], wcs[i % n_copies], wss[i % n_copies], TOPK_K, workspace=tk_ws,
+                                 out=tk_out)
     elif variant == "tail":
         def step(i):
             mtpd.draft_tail(hid, res, g, d["eps"], wcs[i % n_copies], wss[i % n_copies], workspace=wsp, out=out)
@@ -418,11 +454,12 @@ def main() -> int:
     log(f"[bench] timing {K} steps (one HIP graph)")
     ms_step, g1 = timed_graph(step)
     # sanity: the timed outputs are the real ones
+    result = tk_out[1] if variant == "topk" else out[4]
     torch.cuda.synchronize()
-    ref_idx = out[4].clone()
+    ref_idx = result.clone()
     step(0)
     torch.cuda.synchronize()
-    assert torch.equal(ref_idx, out[4]), "graph replay and eager call disagree"
+    assert torch.equal(ref_idx, result), "graph replay and eager call disagree"
     log(f"[bench] timing {K} launches of the roofline kernel (one HIP graph)")
     ms_kernel, g2 = timed_graph(kernel_step)
     del g1, g2
@@ -481,7 +518,7 @@ def main() -> int:
     if variant != "tail":
         config["variant"] = variant
         config.update({"vocab_shards": {"shards": N_SHARDS}, "allreduce_tail": {"partials": N_PARTIALS},
-                       "chain": {"positions": N_CHAIN}}[variant])
+                       "chain": {"positions": N_CHAIN}, "topk": {"k": TOPK_K}}[variant])
     rows_per_step = M * (N_CHAIN if variant == "chain" else 1)
     rec = {
         "metric": METRIC,

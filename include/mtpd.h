@@ -190,6 +190,38 @@ mtpd_status mtpd_argmax_combine(const float *local_max, const int32_t *local_idx
                                 const int64_t *shard_offset, int64_t n_shards, int64_t n_rows,
                                 float *out_max, int32_t *out_idx, void *stream);
 
+/*
+ * Block-scaled FP8 LM head fused with a greedy local top-k
+ * ("Reuse packed FP8 logits inputs", Purpose and Dependencies, for the
+ * logits; "feat(glm52): add checkpoint-native MTP speculative decoding",
+ * Accuracy, where draft and reference distributions are compared by their
+ * top-8 and top-32 sets).
+ *
+ * With z as in mtpd_fp8_lmhead_argmax, for output row i:
+ *   out_idx[i][0..k) = the k vocab rows of largest fp32 z, in descending
+ *                      order of z, equal values in ascending index order
+ *                      (+0 and -0 equal); out_val[i][e] = that z in fp32
+ *                      (-0 returned as +0).  k == 1 gives the argmax.
+ * Logits are never written; per pass of at most 64 rows the streaming
+ * kernel writes one sorted candidate list of k keys per row for each of its
+ * waves (at most V/32 lists) to the workspace and a second launch selects
+ * from them.  More than 64 rows run as several passes, each streaming the
+ * whole weight.
+ *
+ * act, row_index, n_rows, w: as for mtpd_fp8_lmhead_argmax; additionally
+ * w->H <= 8192 and act->rows * w->H <= 2^32.  1 <= k <= 32.  out_val:
+ * [n_rows][k] f32, out_idx: [n_rows][k] int32.  workspace: at least
+ * mtpd_topk_workspace_bytes(n_rows, w->V, k) bytes of device memory, 256-byte
+ * aligned, any contents (nothing needs to be zero).
+ */
+mtpd_status mtpd_fp8_lmhead_topk(const mtpd_qact *act, const int32_t *row_index, int64_t n_rows,
+                                 const mtpd_fp8_weight *w, int64_t k, float *out_val, int32_t *out_idx,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes mtpd_fp8_lmhead_topk needs (a multiple of 256; 0 for
+ * n_rows <= 0 or sizes it does not take). */
+size_t mtpd_topk_workspace_bytes(int64_t n_rows, int64_t V, int64_t k);
+
 /* Bytes of workspace mtpd_fp8_lmhead_argmax / mtpd_draft_tail need for
  * n_rows output rows (a multiple of 256; 0 for n_rows <= 0). */
 size_t mtpd_workspace_bytes(int64_t n_rows);

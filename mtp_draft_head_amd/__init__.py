@@ -22,6 +22,8 @@ Entry points (same names as the C ABI):
       -> norm_quant's outputs for the norm input sum(partials) + residual
   argmax_combine(local_max, local_idx, shard_offsets)
       -> (max f32 [n], global idx int32 [n]) from per-shard pairs [P, n]
+  fp8_lmhead_topk(codes, scales, w_codes, w_scales, k, row_index=None)
+      -> (values f32 [n, k], idx int32 [n, k]), descending
 """
 from __future__ import annotations
 
@@ -34,7 +36,7 @@ import torch
 __all__ = [
     "MtpdError", "MtpdLibraryMissing", "norm_quant", "fp8_lmhead_argmax", "draft_tail",
     "workspace_bytes", "Workspace", "library_path", "lib", "lmhead_plan", "draft_tail_plan",
-    "allreduce_norm_quant", "argmax_combine",
+    "allreduce_norm_quant", "argmax_combine", "fp8_lmhead_topk", "topk_workspace_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -98,6 +100,11 @@ def lib():
                                                 ctypes.POINTER(QAct), P]
         L.mtpd_argmax_combine.restype = ctypes.c_int
         L.mtpd_argmax_combine.argtypes = [P, P, ctypes.POINTER(ctypes.c_int64), I64, I64, P, P, P]
+        L.mtpd_fp8_lmhead_topk.restype = ctypes.c_int
+        L.mtpd_fp8_lmhead_topk.argtypes = [ctypes.POINTER(QAct), P, I64, ctypes.POINTER(FP8Weight), I64, P, P, P,
+                                           ctypes.c_size_t, P]
+        L.mtpd_topk_workspace_bytes.restype = ctypes.c_size_t
+        L.mtpd_topk_workspace_bytes.argtypes = [I64, I64, I64]
         L.mtpd_workspace_bytes.restype = ctypes.c_size_t
         L.mtpd_workspace_bytes.argtypes = [I64]
         L.mtpd_status_name.restype = ctypes.c_char_p
@@ -151,7 +158,9 @@ class Workspace:
         self.buf = None
 
     def get(self, n_rows: int) -> torch.Tensor:
-        need = workspace_bytes(n_rows)
+        return self.get_bytes(workspace_bytes(n_rows))
+
+    def get_bytes(self, need: int) -> torch.Tensor:
         if self.buf is None or self.buf.numel() < need:
             self.buf = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.device)
         return self.buf
@@ -331,3 +340,49 @@ def argmax_combine(local_max, local_idx, shard_offsets, out=None):
         _check(lib().mtpd_argmax_combine(local_max.data_ptr(), local_idx.data_ptr(), arr, P, n,
                                          out_max.data_ptr(), out_idx.data_ptr(), _stream(dev)))
     return out_max, out_idx
+
+
+def topk_workspace_bytes(n_rows: int, V: int, k: int) -> int:
+    return int(lib().mtpd_topk_workspace_bytes(int(n_rows), int(V), int(k)))
+
+
+_topk_ws: dict = {}
+
+
+def fp8_lmhead_topk(codes, scales, w_codes, w_scales, k: int, row_index=None, workspace: Workspace | None = None,
+                    out=None):
+    """Greedy local top-k of the block-scaled FP8 LM head over a packed activation.
+
+    Returns (values float32 [n, k], idx int32 [n, k]), each row in descending
+    order of the fp32 logit, equal values in ascending index order.  The
+    workspace holds candidate lists and needs no zeroing; by default one
+    buffer per device (separate from the argmax workspace) is reused.
+    """
+    _dev(codes, "codes", _U8, 2)
+    _dev(scales, "scales", (torch.float32,), 2)
+    w = _weight(w_codes, w_scales)
+    dev = codes.device
+    A, H = codes.shape
+    if row_index is not None:
+        _dev(row_index, "row_index", (torch.int32,), 1)
+        n = row_index.shape[0]
+        ri = row_index.data_ptr()
+    else:
+        n, ri = A, None
+    k = int(k)
+    if out is None:
+        out_val = torch.empty((n, k), dtype=torch.float32, device=dev)
+        out_idx = torch.empty((n, k), dtype=torch.int32, device=dev)
+    else:
+        out_val, out_idx = out
+    if workspace is None:
+        key = (dev.type, dev.index)
+        if key not in _topk_ws:
+            _topk_ws[key] = Workspace(dev)
+        workspace = _topk_ws[key]
+    ws = workspace.get_bytes(topk_workspace_bytes(n, w.V, k))
+    qa = QAct(codes.data_ptr(), scales.data_ptr(), A, H)
+    with torch.cuda.device(dev):
+        _check(lib().mtpd_fp8_lmhead_topk(ctypes.byref(qa), ri, n, ctypes.byref(w), k, out_val.data_ptr(),
+                                          out_idx.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
+    return out_val, out_idx

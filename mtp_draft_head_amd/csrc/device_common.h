@@ -53,6 +53,7 @@ __device__ __forceinline__ int32_t key_index(uint64_t k) {
 }
 
 __device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t u64_min(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
     uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);

@@ -69,6 +69,16 @@ hipError_t launch_lmhead_stream(const LmheadArgs& a, int nt, int ma, int d, hipS
 bool rows_config_compiled(int mt, int nt, int nw, int d);
 hipError_t launch_lmhead_rows(const LmheadArgs& a, int mt, int nt, int nw, int d, int cus, hipStream_t stream);
 
+// multiprocessor count of the current device (cached per device)
+int device_cus();
+
+// top-k of the LM head (lmhead_stream.hip): at most 64 rows per call, k <= 32;
+// workspace: the candidate lists (no zeroing needed)
+bool topk_supported(int64_t H, int64_t a_rows);
+size_t topk_workspace_bytes(int64_t n_rows, int64_t V, int64_t k);
+hipError_t launch_lmhead_topk(const LmheadArgs& a, int k, float* out_val, int32_t* out_idx, int cus,
+                              hipStream_t stream);
+
 // the fused one-row draft tail (lmhead_stream.hip): M == 1, H <= 6144
 bool use_draft_tail1(int64_t M, int64_t H);
 hipError_t launch_draft_tail1(const uint16_t* hidden, const uint16_t* residual, const float* gamma, float eps,

@@ -250,6 +250,19 @@ __global__ __launch_bounds__(64 * S) void lmhead_argmax_kernel(
     finalize_argmax<64 * S>(ws, n_rows, out_max, out_idx, red);
 }
 
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 namespace {
 
 struct Tile {
@@ -272,18 +285,6 @@ bool compiled(const Tile& t) {
     return false;
 }
 
-int device_cus() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
 
 size_t lds_bytes(const Tile& t, int KB) {
     return (size_t)KB * t.mt * 16 * 4 + (size_t)(t.s - 1) * t.mt * t.nt * 4 * 64 * 4;

@@ -292,6 +292,17 @@ __global__ __launch_bounds__(64) void lmhead_stream_kernel(
 // per-row best keys into a running maximum in LDS (all tiles share the same
 // activation rows); at the end the NW waves' maxima meet, one merge per row,
 // arrival, and the last workgroup decodes.
+//
+// Top-k mode (TOPK): instead of folding per-row maxima, each wave sorts, at
+// the end of every tile, the 32 keys of each activation row over its 32
+// vocab rows with a bitonic network across the 16 lanes of the row's lane
+// group (two keys per lane) and merges them into a running best 32 held in
+// registers the same way.  (Spreading those network steps over the next
+// tile's blocks measured slower: every block's instruction stream grew.)  After the stream each wave writes the best k
+// (<= 32) of every row to its own list in the candidate buffer (no store
+// sits inside the stream, whose waits count vector-memory operations), and
+// topk_merge_kernel selects each row's best k over all lists.  The keys are the argmax epilogue's, so the
+// order is: larger fp32 logit first, lower index first among equal logits.
 // ---------------------------------------------------------------------------
 
 constexpr int kRowsMaxTilesPerWg = 16;   // weight-scale rows staged per workgroup
@@ -307,15 +318,114 @@ constexpr size_t rows_lds_bytes(int mt, int nt, int nw, int d) {
            + (size_t)mt * 16 * kStreamMaxKB * 4;  // activation-scale table
 }
 
-template <int MT, int NT, int NW, int D>
+// Lane exchange inside groups of 16 lanes for a compile-time xor mask:
+// quad permutations (data-parallel moves) for 1 and 2, the LDS swizzle
+// network's bit-mask mode for 4 and 8.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lanes(uint32_t v) {
+    if constexpr (M == 1)
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+    else if constexpr (M == 2)
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+    else
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (M << 10));           // and 0x1F, xor M
+}
+template <int M>
+__device__ __forceinline__ uint64_t xor_lanes_u64(uint64_t v) {
+    return ((uint64_t)xor_lanes<M>((uint32_t)(v >> 32)) << 32) | xor_lanes<M>((uint32_t)v);
+}
+
+// One compare-exchange step of the bitonic network (block size SIZE, partner
+// distance M) on N independent 32-key sets held two per lane by the 16 lanes
+// of each lane group (lane j holds element j in k0[s], element j + 16 in
+// k1[s]); all sets issue their exchanges together so the latencies overlap.
+template <int SIZE, int M, int N>
+__device__ __forceinline__ void bitonic_step(uint64_t (&k0)[N], uint64_t (&k1)[N], int j) {
+    if constexpr (M == 16) {   // elements j and j + 16, one descending block
+#pragma unroll
+        for (int s = 0; s < N; ++s) {
+            const uint64_t hi = u64_max(k0[s], k1[s]), lo = u64_min(k0[s], k1[s]);
+            k0[s] = hi;
+            k1[s] = lo;
+        }
+    } else {
+        // element e keeps the larger key when it is the lower of its pair
+        // inside a descending block (e & SIZE == 0), or the upper inside an
+        // ascending one
+        const bool lower = (j & M) == 0;
+        const bool keep_max0 = lower == ((j & SIZE) == 0);
+        const bool keep_max1 = lower == (((j + 16) & SIZE) == 0);
+        uint64_t o0[N], o1[N];
+#pragma unroll
+        for (int s = 0; s < N; ++s) {
+            o0[s] = xor_lanes_u64<M>(k0[s]);
+            o1[s] = xor_lanes_u64<M>(k1[s]);
+        }
+#pragma unroll
+        for (int s = 0; s < N; ++s) {
+            k0[s] = keep_max0 ? u64_max(k0[s], o0[s]) : u64_min(k0[s], o0[s]);
+            k1[s] = keep_max1 ? u64_max(k1[s], o1[s]) : u64_min(k1[s], o1[s]);
+        }
+    }
+}
+
+// Reverses the 16 lanes of each lane group (data-parallel row mirror).
+__device__ __forceinline__ uint64_t mirror16_u64(uint64_t v) {
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x140, 0xF, 0xF, false);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x140, 0xF, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Merges the descending set (n0, n1) into the descending set (r0, r1),
+// keeping the larger 32 keys in descending order: the elementwise maximum of
+// r and the reversed n is a bitonic sequence holding the 32 largest keys of
+// both, which the last five network steps sort.
+template <int N>
+__device__ __forceinline__ void merge32_desc(uint64_t (&r0)[N], uint64_t (&r1)[N], const uint64_t (&n0)[N],
+                                             const uint64_t (&n1)[N], int j) {
+#pragma unroll
+    for (int s = 0; s < N; ++s) {
+        // element e of the reversed n is n[31 - e]: lane 15 - j, the other half
+        r0[s] = u64_max(r0[s], mirror16_u64(n1[s]));
+        r1[s] = u64_max(r1[s], mirror16_u64(n0[s]));
+    }
+    bitonic_step<32, 16, N>(r0, r1, j);
+    bitonic_step<32, 8, N>(r0, r1, j);
+    bitonic_step<32, 4, N>(r0, r1, j);
+    bitonic_step<32, 2, N>(r0, r1, j);
+    bitonic_step<32, 1, N>(r0, r1, j);
+}
+
+// Sorts N sets of 32 u64 keys (layout as above) into descending order.
+template <int N>
+__device__ __forceinline__ void sort32_desc(uint64_t (&k0)[N], uint64_t (&k1)[N], int j) {
+    bitonic_step<2, 1, N>(k0, k1, j);
+    bitonic_step<4, 2, N>(k0, k1, j);
+    bitonic_step<4, 1, N>(k0, k1, j);
+    bitonic_step<8, 4, N>(k0, k1, j);
+    bitonic_step<8, 2, N>(k0, k1, j);
+    bitonic_step<8, 1, N>(k0, k1, j);
+    bitonic_step<16, 8, N>(k0, k1, j);
+    bitonic_step<16, 4, N>(k0, k1, j);
+    bitonic_step<16, 2, N>(k0, k1, j);
+    bitonic_step<16, 1, N>(k0, k1, j);
+    bitonic_step<32, 16, N>(k0, k1, j);
+    bitonic_step<32, 8, N>(k0, k1, j);
+    bitonic_step<32, 4, N>(k0, k1, j);
+    bitonic_step<32, 2, N>(k0, k1, j);
+    bitonic_step<32, 1, N>(k0, k1, j);
+}
+
+template <int MT, int NT, int NW, int D, bool TOPK>
 __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
     const uint8_t* __restrict__ a_codes, const float* __restrict__ a_scales,
     const int32_t* __restrict__ row_index, int n_rows,
     const uint8_t* __restrict__ w_codes, const float* __restrict__ w_scales, int H,
     int total_tiles,
     float* __restrict__ out_max, int32_t* __restrict__ out_idx,
-    ArgmaxWs ws)
+    ArgmaxWs ws, unsigned long long* __restrict__ cand, int topk)
 {
+    static_assert(!TOPK || NT == 2, "top-k mode sorts 32 vocab rows per wave");
     constexpr int ROWS = MT * 16;
     constexpr int TROWS = NW * NT * 16;      // vocab rows per tile
     constexpr int WSLOT = NT * 2 * 64;       // uint4s per wave per block
@@ -425,6 +535,16 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[mt][nt][i] = 0.f;
 
+    // top-k mode: the running best 32 keys per activation row (layout of
+    // sort32_desc; key 0 is below every real key)
+    constexpr int NS = TOPK ? MT * 4 : 1;
+    uint64_t run0[NS], run1[NS];
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2) {
+        run0[s2] = 0;
+        run1[s2] = 0;
+    }
+
     auto compute = [&](int j, int i, int kb, bool live) {
         const float swl = sw_lds[i][kb];
         const float sw = live ? swl : 0.f;
@@ -449,9 +569,26 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
         }
     };
     // a finished tile: per-row best over this wave's columns, folded into the
-    // wave's running maxima; the accumulators restart
+    // wave's running maxima (top-k mode: the wave's best k per row, written
+    // to its list); the accumulators restart
     auto fold = [&](int i) {
         const int n0 = (b + i * G) * TROWS + wave * NT * 16;
+        if constexpr (TOPK) {
+            const int j = lane & 15;
+            uint64_t k0[NS], k1[NS];   // set mt * 4 + r: activation rows mt * 16 + 4 * (lane / 16) + r
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    k0[mt * 4 + r] = argmax_key(acc[mt][0][r], (uint32_t)(n0 + j));
+                    k1[mt * 4 + r] = argmax_key(acc[mt][1][r], (uint32_t)(n0 + 16 + j));
+                    acc[mt][0][r] = 0.f;
+                    acc[mt][1][r] = 0.f;
+                }
+            sort32_desc<NS>(k0, k1, j);
+            merge32_desc<NS>(run0, run1, k0, k1, j);
+            return;
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -494,6 +631,23 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
     }
     MTPD_WAIT_VM(0);   // the clamped tail refills, before LDS is reused
     __syncthreads();
+    if constexpr (TOPK) {   // this wave's list: the best k of every row
+        const int j = lane & 15;
+        const size_t list = (size_t)b * NW + wave;
+        const size_t n_lists = (size_t)G * NW;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = mt * 16 + 4 * (lane >> 4) + r;
+                if (row < n_rows) {
+                    unsigned long long* dst = cand + ((size_t)row * n_lists + list) * (size_t)topk;
+                    if (j < topk) dst[j] = run0[mt * 4 + r];
+                    if (j + 16 < topk) dst[j + 16] = run1[mt * 4 + r];
+                }
+            }
+        return;   // the lists are merged by topk_merge_kernel
+    }
 
     if (wave == 0) {
         uint64_t old = 0;
@@ -540,16 +694,183 @@ hipError_t launch_lmhead_rows(const LmheadArgs& a, int mt, int nt, int nw, int d
     };
 #define MTPD_X(p, q, r, u)                                                                                    \
     if (mt == p && nt == q && nw == r && d == u) {                                                           \
-        if (!fits(reinterpret_cast<const void*>(&lmhead_stream_rows_kernel<p, q, r, u>)))                   \
+        if (!fits(reinterpret_cast<const void*>(&lmhead_stream_rows_kernel<p, q, r, u, false>)))            \
             return hipErrorInvalidConfiguration;                                                             \
-        hipLaunchKernelGGL((lmhead_stream_rows_kernel<p, q, r, u>), dim3((unsigned)grid), dim3(64 * r), lds,  \
-                           stream, a.a_codes, a.a_scales, a.row_index, (int)a.n_rows, a.w_codes, a.w_scales,  \
-                           (int)a.H, (int)tiles, a.out_max, a.out_idx, argmax_ws(a.workspace, a.n_rows));    \
+        hipLaunchKernelGGL((lmhead_stream_rows_kernel<p, q, r, u, false>), dim3((unsigned)grid), dim3(64 * r), \
+                           lds, stream, a.a_codes, a.a_scales, a.row_index, (int)a.n_rows, a.w_codes,         \
+                           a.w_scales, (int)a.H, (int)tiles, a.out_max, a.out_idx,                            \
+                           argmax_ws(a.workspace, a.n_rows), nullptr, 0);                                     \
         return hipGetLastError();                                                                            \
     }
     MTPD_ROWS_CONFIGS(MTPD_X)
 #undef MTPD_X
     return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Top-k (k <= 32): the rows kernel in top-k mode writes, per activation row,
+// one sorted list of the best k keys for every wave of its (persistent)
+// grid.  One
+// workgroup per row then bounds the row's k-th key from below by the k-th
+// largest of its threads' best list heads, gathers every key at or above
+// that bound into LDS (lists are sorted, so each is read only down to its
+// first smaller key) and places each gathered key by counting the larger
+// ones.  If nearly equal logits put more than 2048 keys above the bound, a
+// slower selection (private best-32 per thread, then k rounds of a
+// workgroup maximum) takes over.
+// ---------------------------------------------------------------------------
+
+constexpr int kTopkMax = 32;
+constexpr int kTopkRows = 64;      // activation rows per rows-kernel pass
+constexpr int kTopkListRows = 128; // vocab rows per tile (NT = 2, NW = 4)
+
+__global__ __launch_bounds__(256) void topk_merge_kernel(const unsigned long long* __restrict__ cand, int n_lists,
+                                                         int k, float* __restrict__ out_val,
+                                                         int32_t* __restrict__ out_idx)
+{
+    constexpr int kCap = 2048;   // candidates kept in LDS for the rank selection
+    __shared__ unsigned long long buf[kCap];
+    __shared__ unsigned long long heads[256];
+    __shared__ unsigned long long wred[4];
+    __shared__ unsigned long long thr;
+    __shared__ int count;
+    const int row = (int)blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const unsigned long long* base = cand + (size_t)row * (size_t)n_lists * (size_t)k;
+    float* vrow = out_val + (size_t)row * k;
+    int32_t* irow = out_idx + (size_t)row * k;
+
+    // 1. a lower bound T of the row's k-th key: each thread's best list head
+    //    (lists are sorted), and the k-th largest of those 256 maxima (k
+    //    distinct keys are at least that large).  Keys are unique and
+    //    nonzero; a thread without lists offers 0.
+    uint64_t h = 0;
+    for (int l = t; l < n_lists; l += 256) h = u64_max(h, base[(size_t)l * k]);
+    heads[t] = h;
+    if (t == 0) {
+        thr = 0;
+        count = 0;
+    }
+    __syncthreads();
+    if (h != 0) {
+        int rank = 0;
+        for (int q = 0; q < 256; ++q) rank += heads[q] > h ? 1 : 0;
+        if (rank == k - 1) thr = h;
+    }
+    __syncthreads();
+    const uint64_t T = thr;
+
+    // 2. every key >= T into LDS (a list is left at its first smaller key)
+    for (int l = t; l < n_lists; l += 256) {
+        const unsigned long long* lst = base + (size_t)l * k;
+        for (int e = 0; e < k; ++e) {
+            const uint64_t x = lst[e];
+            if (x < T) break;
+            const int pos = atomicAdd(&count, 1);
+            if (pos < kCap) buf[pos] = x;
+        }
+    }
+    __syncthreads();
+    const int n = count;
+
+    if (n <= kCap) {
+        // 3. rank selection: a key's position is the number of larger keys
+        for (int c = t; c < n; c += 256) {
+            const uint64_t x = buf[c];
+            int rank = 0;
+            for (int q = 0; q < n; ++q) rank += buf[q] > x ? 1 : 0;
+            if (rank < k) {
+                vrow[rank] = key_value(x);
+                irow[rank] = key_index(x);
+            }
+        }
+        return;
+    }
+
+    // 3'. too many keys >= T (nearly equal logits): a private best-32 per
+    //     thread over them, then the k best of the 256 private heads
+    uint64_t best[kTopkMax];
+#pragma unroll
+    for (int p = 0; p < kTopkMax; ++p) best[p] = 0;
+    for (int l = t; l < n_lists; l += 256) {
+        const unsigned long long* lst = base + (size_t)l * k;
+        for (int e = 0; e < k; ++e) {
+            uint64_t x = lst[e];
+            if (x < T || x <= best[kTopkMax - 1]) break;   // sorted list: nothing after it enters either
+#pragma unroll
+            for (int p = 0; p < kTopkMax; ++p) {
+                const uint64_t hi = u64_max(best[p], x);
+                x = u64_min(best[p], x);
+                best[p] = hi;
+            }
+        }
+    }
+    for (int e = 0; e < k; ++e) {
+        uint64_t m = best[0];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = u64_max(m, shfl_xor_u64(m, off));
+        if (lane == 0) wred[wave] = m;
+        __syncthreads();
+        const uint64_t bm = u64_max(u64_max(wred[0], wred[1]), u64_max(wred[2], wred[3]));
+        __syncthreads();   // every thread has read wred before the next round rewrites it
+        if (best[0] == bm) {   // keys are unique: exactly one thread holds the winner
+#pragma unroll
+            for (int p = 0; p < kTopkMax - 1; ++p) best[p] = best[p + 1];
+            best[kTopkMax - 1] = 0;
+        }
+        if (t == 0) {
+            vrow[e] = key_value(bm);
+            irow[e] = key_index(bm);
+        }
+    }
+}
+
+bool topk_supported(int64_t H, int64_t a_rows) { return H <= kStreamMaxH && a_rows * H <= ((int64_t)1 << 32); }
+
+size_t topk_workspace_bytes(int64_t n_rows, int64_t V, int64_t k) {
+    if (n_rows <= 0) return 0;
+    const int64_t rows = std::min<int64_t>(n_rows, kTopkRows);
+    const int64_t lists = V / kTopkListRows * 4;
+    return ((size_t)rows * (size_t)lists * (size_t)k * 8 + 255) & ~(size_t)255;
+}
+
+hipError_t launch_lmhead_topk(const LmheadArgs& a, int k, float* out_val, int32_t* out_idx, int cus,
+                              hipStream_t stream) {
+    const int64_t tiles = a.V / kTopkListRows;
+    if (a.n_rows < 1 || a.n_rows > kTopkRows || k < 1 || k > kTopkMax || tiles > 0x7FFFFFFF ||
+        !topk_supported(a.H, a.a_rows))
+        return hipErrorInvalidValue;
+    int64_t grid = std::min<int64_t>(tiles, cus);
+    grid = std::max<int64_t>(grid, (tiles + kRowsMaxTilesPerWg - 1) / kRowsMaxTilesPerWg);
+    const int mt = a.n_rows <= 32 ? 2 : 4;
+    const size_t lds = (size_t)(16 * mt) * (size_t)(a.H / kBlock) * sizeof(float);
+    unsigned long long* cand = reinterpret_cast<unsigned long long*>(a.workspace);
+    auto fits = [&](const void* kernel) {
+        hipFuncAttributes attr;
+        if (hipFuncGetAttributes(&attr, kernel) != hipSuccess) return false;
+        int dev = 0, cap = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cap, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            return false;
+        return attr.sharedSizeBytes + lds <= (size_t)cap;
+    };
+#define MTPD_TOPK_LAUNCH(M)                                                                                   \
+    {                                                                                                          \
+        if (!fits(reinterpret_cast<const void*>(&lmhead_stream_rows_kernel<M, 2, 4, 3, true>)))              \
+            return hipErrorInvalidConfiguration;                                                               \
+        hipLaunchKernelGGL((lmhead_stream_rows_kernel<M, 2, 4, 3, true>), dim3((unsigned)grid), dim3(256), lds, \
+                           stream, a.a_codes, a.a_scales, a.row_index, (int)a.n_rows, a.w_codes, a.w_scales,    \
+                           (int)a.H, (int)tiles, nullptr, nullptr, ArgmaxWs{}, cand, k);                       \
+    }
+    if (mt == 2)
+        MTPD_TOPK_LAUNCH(2)
+    else
+        MTPD_TOPK_LAUNCH(4)
+#undef MTPD_TOPK_LAUNCH
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)a.n_rows), dim3(256), 0, stream, cand, (int)(grid * 4), k,
+                       out_val, out_idx);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

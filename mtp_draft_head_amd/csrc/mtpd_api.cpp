@@ -132,7 +132,7 @@ const char* mtpd_last_error(void) { return g_err; }
 
 void mtpd_clear_error(void) { g_err[0] = 0; }
 
-int mtpd_abi_version(void) { return 3; }
+int mtpd_abi_version(void) { return 4; }
 
 const char* mtpd_lmhead_plan(int64_t n_rows, int64_t V, int64_t H) {
     thread_local char buf[160];
@@ -311,6 +311,71 @@ mtpd_status mtpd_argmax_combine(const float* local_max, const int32_t* local_idx
     return hip_status(mtpd::launch_argmax_combine(local_max, local_idx, offs, (int)n_shards, n_rows, out_max, out_idx,
                                                   (hipStream_t)stream),
                       "argmax_combine launch");
+}
+
+size_t mtpd_topk_workspace_bytes(int64_t n_rows, int64_t V, int64_t k) {
+    if (n_rows <= 0 || n_rows > kMaxRows || k < 1 || k > 32 || V < mtpd::kBlock || V > kMaxV || V % mtpd::kBlock)
+        return 0;
+    return mtpd::topk_workspace_bytes(n_rows, V, k);
+}
+
+mtpd_status mtpd_fp8_lmhead_topk(const mtpd_qact* act, const int32_t* row_index, int64_t n_rows,
+                                 const mtpd_fp8_weight* w, int64_t k, float* out_val, int32_t* out_idx,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (!act) return fail(MTPD_ERR_NULL, "act descriptor is NULL");
+    if (n_rows < 0 || n_rows > kMaxRows) return fail(MTPD_ERR_SHAPE, "n_rows=%lld out of [0, 2^24]", (long long)n_rows);
+    if (k < 1 || k > 32) return fail(MTPD_ERR_SHAPE, "k=%lld out of [1, 32]", (long long)k);
+    mtpd_status st = check_H(act->cols);
+    if (st != MTPD_OK) return st;
+    st = check_weight(w, act->cols);
+    if (st != MTPD_OK) return st;
+    if (n_rows == 0) return MTPD_OK;
+    if (act->rows < 1 || act->rows > kMaxRows)
+        return fail(MTPD_ERR_SHAPE, "act rows=%lld out of [1, 2^24]", (long long)act->rows);
+    if (!row_index && n_rows > act->rows)
+        return fail(MTPD_ERR_SHAPE, "n_rows=%lld exceeds act rows=%lld with no row_index", (long long)n_rows,
+                    (long long)act->rows);
+    if (!mtpd::topk_supported(act->cols, act->rows))
+        return fail(MTPD_ERR_SHAPE, "top-k takes H <= 8192 and act rows * H <= 2^32 (H=%lld, rows=%lld)",
+                    (long long)act->cols, (long long)act->rows);
+    if (!act->codes || !act->scales) return fail(MTPD_ERR_NULL, "act codes/scales pointer is NULL");
+    if (!out_val || !out_idx) return fail(MTPD_ERR_NULL, "out_val/out_idx is NULL");
+    if (!aligned(act->codes, 16)) return fail(MTPD_ERR_ALIGN, "act codes not 16-byte aligned");
+    if (!aligned(act->scales, 4)) return fail(MTPD_ERR_ALIGN, "act scales not 4-byte aligned");
+    if (row_index && !aligned(row_index, 4)) return fail(MTPD_ERR_ALIGN, "row_index not 4-byte aligned");
+    if (!aligned(out_val, 4) || !aligned(out_idx, 4)) return fail(MTPD_ERR_ALIGN, "out_val/out_idx not 4-byte aligned");
+    const size_t need = mtpd::topk_workspace_bytes(n_rows, w->V, k);
+    if (!workspace || workspace_bytes < need)
+        return fail(MTPD_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", workspace_bytes, workspace,
+                    need);
+    if (!aligned(workspace, 256)) return fail(MTPD_ERR_ALIGN, "workspace not 256-byte aligned");
+    const size_t ah = (size_t)act->rows * (size_t)act->cols;
+    const size_t nk = (size_t)n_rows * (size_t)k;
+    const Range outs[] = {{out_val, nk * 4, "out_val"}, {out_idx, nk * 4, "out_idx"}, {workspace, need, "workspace"}};
+    const Range ins[] = {{act->codes, ah, "act.codes"},
+                         {act->scales, ah / 128 * 4, "act.scales"},
+                         {row_index, row_index ? (size_t)n_rows * 4 : 0, "row_index"},
+                         {w->codes, (size_t)w->V * (size_t)w->H, "w.codes"},
+                         {w->scales, (size_t)(w->V / 128) * (size_t)(w->H / 128) * 4, "w.scales"}};
+    st = check_alias(outs, 3, ins, 5);
+    if (st != MTPD_OK) return st;
+    const int64_t KB = act->cols / 128;
+    const int cus = mtpd::device_cus();
+    for (int64_t c = 0; c < n_rows; c += 64) {
+        const int64_t n = n_rows - c < 64 ? n_rows - c : 64;
+        mtpd::LmheadArgs a{act->codes, act->scales, row_index ? row_index + c : nullptr, n, act->rows,
+                           w->codes, w->scales, w->V, w->H, nullptr, nullptr, workspace};
+        if (!row_index) {   // rows c .. c + n - 1 of the activation
+            a.a_codes = act->codes + (size_t)c * (size_t)act->cols;
+            a.a_scales = act->scales + (size_t)c * (size_t)KB;
+            a.a_rows = act->rows - c;
+        }
+        st = hip_status(mtpd::launch_lmhead_topk(a, (int)k, out_val + (size_t)c * (size_t)k,
+                                                 out_idx + (size_t)c * (size_t)k, cus, (hipStream_t)stream),
+                        "lmhead_topk launch");
+        if (st != MTPD_OK) return st;
+    }
+    return MTPD_OK;
 }
 
 }  // extern "C"

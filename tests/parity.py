@@ -89,3 +89,36 @@ def check_argmax(gpu_max, gpu_idx, ora, logit_row=None):
         z = logit_row(int(i))
         assert z[gpu_idx[i]] >= z1[i] - NEAR_TIE_RTOL * abs(z1[i]), f"row {i}: index outside near-tie band"
     return dict(max_rel=worst, near_tie_rows=int(np.sum(near)), near_tie_differ=int(np.sum(diff & near)))
+
+
+def check_topk(gpu_val, gpu_idx, ora_val, ora_idx, logit_row):
+    """Top-k lists against the oracle's, row by row.
+
+    The GPU list must be in non-increasing value order with distinct indices;
+    its values must match the oracle's sorted values position by position
+    within MAX_RTOL; an index may differ from the oracle's only inside the
+    near-tie band: its oracle logit lies within NEAR_TIE_RTOL |z| of the
+    oracle's value at that position.  logit_row(i) -> the oracle's fp64 logits
+    of row i (called only for rows with a differing index)."""
+    gv = np.asarray(gpu_val, np.float32).astype(np.float64)
+    gi = np.asarray(gpu_idx, np.int64)
+    ov = np.asarray(ora_val, np.float32).astype(np.float64)
+    oi = np.asarray(ora_idx, np.int64)
+    assert gv.shape == ov.shape and gi.shape == oi.shape
+    n, k = gv.shape
+    rel = np.abs(gv - ov) / np.maximum(np.abs(ov), 1e-30)
+    worst = float(rel.max()) if rel.size else 0.0
+    assert worst <= MAX_RTOL, f"top-k value rel err {worst:.3e}"
+    assert np.all(np.diff(gv, axis=1) <= 0), "top-k values not in descending order"
+    differ = 0
+    for i in range(n):
+        assert len(set(gi[i].tolist())) == k, f"row {i}: repeated index"
+        if np.array_equal(gi[i], oi[i]):
+            continue
+        z = logit_row(i)
+        for e in np.nonzero(gi[i] != oi[i])[0]:
+            differ += 1
+            assert abs(z[gi[i, e]] - ov[i, e]) <= NEAR_TIE_RTOL * abs(ov[i, e]), (
+                f"row {i} position {e}: index {gi[i, e]} (logit {z[gi[i, e]]}) outside the near-tie band of "
+                f"{ov[i, e]}")
+    return dict(max_rel=worst, near_tie_differ=differ)

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(L):
     assert {"mtpd_norm_quant", "mtpd_fp8_lmhead_argmax", "mtpd_draft_tail", "mtpd_workspace_bytes",
             "mtpd_status_name", "mtpd_last_error", "mtpd_clear_error", "mtpd_abi_version",
             "mtpd_lmhead_plan", "mtpd_draft_tail_plan", "mtpd_allreduce_norm_quant",
-            "mtpd_argmax_combine"} <= set(names)
+            "mtpd_argmax_combine", "mtpd_fp8_lmhead_topk", "mtpd_topk_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -46,7 +46,7 @@ def test_status_names_and_version(L):
         "MTPD_OK", "MTPD_ERR_NULL", "MTPD_ERR_SHAPE", "MTPD_ERR_ALIGN", "MTPD_ERR_ALIAS",
         "MTPD_ERR_WORKSPACE", "MTPD_ERR_HIP"]
     assert L.mtpd_status_name(99).decode() == "MTPD_UNKNOWN"
-    assert L.mtpd_abi_version() == 3
+    assert L.mtpd_abi_version() == 4
 
 
 def test_workspace_bytes(L):
@@ -191,6 +191,41 @@ def test_argmax_combine_validation(L):
     assert cb(omax=A + 8) == ALIAS                        # output inside local_max ([2][4] f32)
     assert cb(oidx=A + 0x2008) == ALIAS                   # the two outputs overlap
     assert cb(rows=0, lmax=None, lidx=None, omax=None, oidx=None) == OK
+
+
+def test_topk_workspace_bytes(L):
+    # one pass of at most 64 rows: rows x (V / 32 lists) x k keys x 8 bytes, padded to 256
+    assert L.mtpd_topk_workspace_bytes(1, 18944, 8) == -(-1 * (18944 // 32) * 8 * 8 // 256) * 256
+    assert L.mtpd_topk_workspace_bytes(64, 151552, 32) == 64 * (151552 // 32) * 32 * 8
+    assert L.mtpd_topk_workspace_bytes(300, 1024, 4) == L.mtpd_topk_workspace_bytes(64, 1024, 4)
+    assert L.mtpd_topk_workspace_bytes(0, 1024, 4) == 0
+    assert L.mtpd_topk_workspace_bytes(4, 1024, 0) == 0
+    assert L.mtpd_topk_workspace_bytes(4, 1024, 33) == 0
+    assert L.mtpd_topk_workspace_bytes(4, 1000, 4) == 0
+
+
+def test_topk_validation(L):
+    def tk(M=4, H=256, V=1024, k=8, act_codes=A, w_codes=A + 0x1000000, ws=A + 0x4000000, ws_bytes=None,
+           out_val=A + 0x3000000, out_idx=A + 0x3100000):
+        qa = QAct(act_codes, A + 0x100000, M, H)
+        w = FP8Weight(w_codes, A + 0x2000000, V, H)
+        if ws_bytes is None:
+            ws_bytes = max(L.mtpd_topk_workspace_bytes(M, V, k), 256)
+        L.mtpd_clear_error()
+        return L.mtpd_fp8_lmhead_topk(ctypes.byref(qa), None, M, ctypes.byref(w), k, out_val, out_idx, ws,
+                                      ws_bytes, None)
+    assert tk(k=0) == SHAPE
+    assert tk(k=33) == SHAPE
+    assert tk(H=16384) == SHAPE                          # beyond the streaming kernel's H
+    assert tk(V=1000) == SHAPE
+    assert tk(act_codes=None) == NULL
+    assert tk(out_val=None) == NULL
+    assert tk(ws=None) == WORKSPACE
+    assert tk(ws_bytes=256) == WORKSPACE
+    assert tk(ws=A + 0x4000000 + 64) == ALIGN
+    assert tk(out_idx=A + 0x3000000 + 16) == ALIAS       # the two outputs overlap
+    assert tk(out_val=A + 0x1000000) == ALIAS            # output over the weight codes
+    assert tk(M=0) == OK
 
 
 def test_binding_refuses_cpu_tensors():
