@@ -125,10 +125,12 @@ __global__ __launch_bounds__(64) void lmhead_stream_kernel(
     __shared__ __align__(16) uint4 ring[D * SLOT];
     __shared__ unsigned long long red[64];
     __shared__ int last_flag;
-    // scales, copied once: sa_lds[r][kb] for fragment row r (rows past the
-    // last activation row repeat it), sw_lds[kb] for the tiles' 128-row block;
-    // entries past KB repeat the last block
-    __shared__ __align__(16) float sa_lds[16 * kStreamMaxKB];
+    // scales, copied once: sa_lds[kb][r] for fragment row r (rows past the
+    // last activation row repeat it; block-major, so a lane's four rows of a
+    // block are one 16-byte read and the four lane groups hit distinct
+    // banks), sw_lds[kb] for the tiles' 128-row block; entries past KB repeat
+    // the last block
+    __shared__ __align__(16) float sa_lds[kStreamMaxKB * 16];
     __shared__ __align__(16) float sw_lds[kStreamMaxKB];
 
     const int lane = threadIdx.x;
@@ -188,13 +190,12 @@ __global__ __launch_bounds__(64) void lmhead_stream_kernel(
 
     // scale reads: rows 4 * fg + i of block kb; padding blocks (kb >= KB) get
     // a zero factor
-    const float* sar = &sa_lds[4 * fg * kStreamMaxKB];
     auto compute = [&](int j, int kb) {
         const int kc = min(kb, kStreamMaxKB - 1);
         const float swl = sw_lds[kc];
         const float sw = kb < KB ? swl : 0.f;
-        const float4 f = make_float4(sar[kc] * sw, sar[kStreamMaxKB + kc] * sw, sar[2 * kStreamMaxKB + kc] * sw,
-                                     sar[3 * kStreamMaxKB + kc] * sw);
+        const float4 sa4 = *reinterpret_cast<const float4*>(&sa_lds[kc * 16 + 4 * fg]);
+        const float4 f = make_float4(sa4.x * sw, sa4.y * sw, sa4.z * sw, sa4.w * sw);
         const uint4* ta = &ring[j * SLOT + NT * 128];
         const v8i af = make_frag(ta[apos0], ta[apos1]);
 #pragma unroll
@@ -208,25 +209,26 @@ __global__ __launch_bounds__(64) void lmhead_stream_kernel(
         }
     };
 
-    // prologue: the scales (16 activation rows and the weight-scale row, 64
-    // blocks each), then the first D ring blocks.  All are copies into LDS,
-    // older than any ring block, so the first ring wait covers them.  The
-    // gathered row numbers are loaded first and waited for here: a register
-    // load completing after the copies were issued would make the compiler
-    // wait for those too.
-    uint32_t srow[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    // prologue: the activation scales of the 16 fragment rows, loaded into
+    // registers and stored block-major (register loads, all completed here,
+    // before the first ring copy is issued: a register load completing after
+    // the copies were issued would make the compiler wait for those too);
+    // then the weight-scale row and the first D ring blocks, copies into LDS
+    // older than any ring block, so the first ring wait covers them
+    {
+        const int r = lane & 15;
         const int mr = min(r, n_rows - 1);
-        srow[r] = (uint32_t)(row_index ? row_index[mr] : mr);
+        const uint32_t srow = (uint32_t)(row_index ? row_index[mr] : mr);
+        float v[kStreamMaxKB / 4];
+#pragma unroll
+        for (int i = 0; i < kStreamMaxKB / 4; ++i) v[i] = a_scales[srow * (uint32_t)KB + min((lane >> 4) + 4 * i, KB - 1)];
+#pragma unroll
+        for (int i = 0; i < kStreamMaxKB / 4; ++i) sa_lds[((lane >> 4) + 4 * i) * 16 + r] = v[i];
     }
     MTPD_WAIT_VM(0);
     asm volatile("" ::: "memory");
     {
         const uint32_t kl = (uint32_t)min(lane, KB - 1);
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            lds_copy4(a_scales, (srow[r] * (uint32_t)KB + kl) * 4u, lds_addr(&sa_lds[r * kStreamMaxKB]));
         lds_copy4(w_scales + (size_t)(n0 >> 7) * KB, kl * 4u, lds_addr(sw_lds));
     }
 #pragma unroll
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
     __shared__ __align__(16) float sw_lds[kRowsMaxTilesPerWg][kStreamMaxKB];
     __shared__ unsigned long long red[64 * NW];   // running per-row maxima, one set per wave
     __shared__ int last_flag;
-    extern __shared__ __align__(16) float sa_lds[];   // [ROWS][KB]
+    extern __shared__ __align__(16) float sa_lds[];   // [KB][ROWS], block-major
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -471,17 +473,19 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
         const int m = min(8 * p + (lane >> 3), n_rows - 1);
         aoff[i] = (uint32_t)(row_index ? row_index[m] : m) * (uint32_t)H + (uint32_t)ring_pos(r16, lane & 7) * 16u;
     }
-    // activation-scale rows this wave copies, loaded (and waited for) before
-    // any copy is issued
-    constexpr int RPW = ROWS / NW;
-    uint32_t srow[RPW];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int m = min(wave * RPW + i, n_rows - 1);
-        srow[i] = (uint32_t)(row_index ? row_index[m] : m);
+    // the activation-scale table, block-major [KB][ROWS] so a lane's four
+    // fragment rows of a block are one 16-byte read and the four lane groups
+    // hit distinct banks: thread t fills row t % ROWS.  Register loads, all
+    // completed (and the table published) before any copy is issued.
+    {
+        constexpr int THREADS = 64 * NW;
+        static_assert(THREADS % ROWS == 0, "each thread fills one row of the table");
+        const int row = t % ROWS;
+        const int m = min(row, n_rows - 1);
+        const uint32_t srow = (uint32_t)(row_index ? row_index[m] : m);
+        for (int kb = t / ROWS; kb < KB; kb += THREADS / ROWS) sa_lds[kb * ROWS + row] = a_scales[srow * (uint32_t)KB + kb];
     }
-    MTPD_WAIT_VM(0);
-    asm volatile("" ::: "memory");
+    __syncthreads();
 
     const int fr = lane & 15, fg = lane >> 4;
     const int fpos0 = fr * 8 + ring_pos(fr, fg);
@@ -504,11 +508,9 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
             lds_copy16(ab, aoff[i2], aring0 + (uint32_t)(j * ASLOT + (wave + NW * i2) * 64) * 16u);
     };
 
-    // prologue: scale tables (lanes past KB idle), then units 0..D-2
+    // prologue: the weight-scale rows of the workgroup's tiles (lanes past
+    // KB idle), then units 0..D-2
     if (lane < KB) {
-#pragma unroll
-        for (int i = 0; i < RPW; ++i)
-            lds_copy4(a_scales, (srow[i] * (uint32_t)KB + (uint32_t)lane) * 4u, lds_addr(&sa_lds[(wave * RPW + i) * KB]));
         for (int i = wave; i < ntiles; i += NW)
             lds_copy4(w_scales + (size_t)((b + i * G) * TROWS >> 7) * KB, (uint32_t)lane * 4u, lds_addr(&sw_lds[i][0]));
     }
@@ -556,8 +558,8 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
         for (int mt = 0; mt < MT; ++mt) {
             const uint4* ta = &aring[j * ASLOT + mt * 128];
             const v8i af = make_frag(ta[fpos0], ta[fpos1]);
-            const float* sr = &sa_lds[(mt * 16 + 4 * fg) * KB + kb];
-            const float f0 = sr[0] * sw, f1 = sr[KB] * sw, f2 = sr[2 * KB] * sw, f3 = sr[3 * KB] * sw;
+            const float4 sa4 = *reinterpret_cast<const float4*>(&sa_lds[kb * ROWS + mt * 16 + 4 * fg]);
+            const float f0 = sa4.x * sw, f1 = sa4.y * sw, f2 = sa4.z * sw, f3 = sa4.w * sw;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const v4f p = mfma_e4m3(af, bf[nt]);
