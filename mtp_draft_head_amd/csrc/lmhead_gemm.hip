@@ -60,11 +60,12 @@ struct Stage {
 #define MTPD_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
 // Position of chunk c (16 bytes, 0..3) of row r's 64-byte K half inside the
-// row's slot of a piece.  The XOR makes the fragment reads conflict-free:
-// the MFMA lanes reading one LDS cycle's worth of 16-byte words (8 or 16
-// consecutive lanes, rows r..r+7 or r..r+15 of one K group) land on distinct
-// bank groups for either LDS bank count.
-__device__ __forceinline__ int piece_chunk(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
+// row's slot of a piece.  A fragment read has lane l on row l % 16 and K
+// group l / 16; with the chunk moved to c ^ ((r >> 1) & 3) the hardware's
+// bank-conflict counter reads zero for that read on gfx950 (an LDS probe of
+// this exact pattern; c ^ ((r >> 1) ^ (r >> 3)) & 3, c ^ (r & 3) and no
+// swizzle all counted conflicts).
+__device__ __forceinline__ int piece_chunk(int r, int c) { return c ^ ((r >> 1) & 3); }
 
 // Workgroup barrier without a memory fence: the LDS-DMA copies a wave must
 // have finished are waited for explicitly (MTPD_WAIT_VMCNT) just before, and

@@ -61,11 +61,12 @@ __device__ __forceinline__ void wait_vm(int n) {
 }
 
 // Position of 16-byte chunk c (0..7) of tile row r inside the row's 128-byte
-// LDS slot.  A fragment read has each group of 8 (or 16) consecutive lanes on
-// 8 (16) consecutive rows and one K group: with s(r) = (r ^ (r >> 3)) & 7 the
-// rows of such a group land on distinct 16-byte bank groups whether the LDS
-// serves 128 or 256 bytes per cycle.
-__device__ __forceinline__ int ring_pos(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+// LDS slot.  A fragment read has lane l on row l % 16 and K group l / 16;
+// with the chunk moved to c ^ (r & 7) the hardware's bank-conflict counter
+// reads zero for that read on gfx950 (an LDS probe of this exact pattern:
+// the earlier c ^ ((r ^ (r >> 3)) & 7) counted 4 conflict cycles per read,
+// no swizzle 12).
+__device__ __forceinline__ int ring_pos(int r, int c) { return c ^ (r & 7); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
