@@ -947,17 +947,13 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
         for (int q = 0; q < 2; ++q) lds_copy16_stream(wb, woff[q], ring0 + (uint32_t)(j * SLOT + q * 64) * 16u);
     };
 
-    // 1. per wave: the weight-scale row and the first D blocks of its range
-    if (nb > 0) {
-        lds_copy4(w_scales + (size_t)(n0 >> 7) * KB, (uint32_t)min(lane, KB - 1) * 4u, lds_addr(&sw_lds[wave][0]));
-#pragma unroll
-        for (int j = 0; j < D; ++j) refill(j, kb0 + min(j, nb - 1));
-    }
-
-    // 2. norm_quant_kernel's body for the row (thread t owns columns
-    //    k*2048 + 8t .. +7 of each step); codes and scales go to LDS.  All
-    //    input loads (norm weight included) issue before any use: clamped
-    //    addresses, zeroed values, no branch.
+    // 1. the row's norm inputs (thread t owns columns k*2048 + 8t .. +7 of
+    //    each step): all loads issue before any use (clamped addresses,
+    //    zeroed values, no branch) and are waited for here, before any weight
+    //    copy is issued, so the wait does not include the ring (the counter
+    //    is in order: a load issued after the copies would complete only
+    //    after them, and the whole grid's first copies take microseconds to
+    //    drain from HBM)
     uint4 hraw[NSTEP], rraw[NSTEP];
     float4 graw[NSTEP][2];
 #pragma unroll
@@ -968,7 +964,18 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
         graw[k][0] = *reinterpret_cast<const float4*>(gamma + cc);
         graw[k][1] = *reinterpret_cast<const float4*>(gamma + cc + 4);
     }
+    MTPD_WAIT_VM(0);
     asm volatile("" ::: "memory");
+
+    // 2. per wave: the weight-scale row and the first D blocks of its range,
+    //    in flight while the norm runs
+    if (nb > 0) {
+        lds_copy4(w_scales + (size_t)(n0 >> 7) * KB, (uint32_t)min(lane, KB - 1) * 4u, lds_addr(&sw_lds[wave][0]));
+#pragma unroll
+        for (int j = 0; j < D; ++j) refill(j, kb0 + min(j, nb - 1));
+    }
+
+    // 3. norm_quant_kernel's body for the row; codes and scales go to LDS
     float sv[NSTEP][8];
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k) {
@@ -1032,7 +1039,7 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
     }
     __syncthreads();   // also completes every wave's ring prologue
 
-    // 3. the weight stream over this wave's blocks; fragment rows all read
+    // 4. the weight stream over this wave's blocks; fragment rows all read
     //    the packed row
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     const float* swv = &sw_lds[wave][0];
@@ -1065,7 +1072,7 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
         }
     }
 
-    // 4. partials meet in LDS, summed in wave order (row 0 sits in lanes
+    // 5. partials meet in LDS, summed in wave order (row 0 sits in lanes
     //    0..15, element 0)
     if (wave > 0) {
 #pragma unroll
