@@ -81,6 +81,7 @@ hipError_t launch_lmhead_topk(const LmheadArgs& a, int k, float* out_val, int32_
 
 // the fused one-row draft tail (lmhead_stream.hip): M == 1, H <= 6144
 bool use_draft_tail1(int64_t M, int64_t H);
+int64_t draft_tail1_grid(int64_t V);   // workgroups of the fused one-row launch
 hipError_t launch_draft_tail1(const uint16_t* hidden, const uint16_t* residual, const float* gamma, float eps,
                               int64_t H, const uint8_t* w_codes, const float* w_scales, int64_t V,
                               uint16_t* out_hidden, uint8_t* codes, float* scales, float* out_max, int32_t* out_idx,

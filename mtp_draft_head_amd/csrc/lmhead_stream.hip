@@ -879,22 +879,28 @@ hipError_t launch_lmhead_topk(const LmheadArgs& a, int k, float* out_val, int32_
 // ---------------------------------------------------------------------------
 // The whole draft tail for one row (decode at concurrency 1) in one kernel.
 //
-// A workgroup is four waves on one 16-row weight tile, each wave streaming a
-// quarter of the K blocks through its own ring (the streaming kernel's
-// schedule); partial accumulators meet in LDS and are summed in wave order.
-// Before that, every workgroup recomputes the row's residual add + RMSNorm +
-// E4M3 packing itself (24 KB of bf16 input plus the norm weight, L2-resident
-// after the first workgroup of each XCD), so no second launch and no
-// cross-workgroup hand-off is needed.  That part is norm_quant_kernel's body
-// for one row, thread for thread (same per-thread fma order, same butterfly,
-// same fixed-order sum of the four wave totals), so the packed row and the
-// bf16 hidden are bit-identical to the two-kernel path; the packed row stays
-// in LDS as the MFMA activation (every fragment row reads row 0) and one
-// workgroup writes the row's outputs after its stream has finished.
+// One resident workgroup of four waves per CU takes the 16-row weight tiles
+// t = blockIdx, blockIdx + G, ...; each wave streams a quarter of every
+// tile's K blocks through its own ring, and all of the workgroup's tiles form
+// one continuous stream per wave, so the rings never drain between tiles.
+// At the end of each tile the four partial sums meet in LDS and are added in
+// wave order into a running per-lane best key.
+//
+// Before the stream the workgroup computes the row's residual add + RMSNorm
+// + E4M3 packing itself (norm_quant_kernel's body for one row, thread for
+// thread: same per-thread fma order, same butterfly, same fixed-order sum of
+// the four wave totals), so the packed row and the bf16 hidden are
+// bit-identical to the two-kernel path; the packed row stays in LDS as the
+// MFMA activation (every fragment row reads row 0).  The norm inputs (bf16
+// hidden and residual, fp32 norm weight) reach LDS by direct copies issued
+// before the weight ring, so the norm waits only for them while the ring
+// fills (the vector-memory counter is in order).  Workgroup 0 writes the
+// row's outputs after its stream.
 // ---------------------------------------------------------------------------
 
-constexpr int kTail1MaxH = 6144;   // NSTEP <= 3: the row's inputs stay in registers
-constexpr int kTail1D = 3;         // ring depth per wave
+constexpr int kTail1MaxH = 6144;   // NSTEP <= 3 steps of 2048 columns
+constexpr int kTail1D = 8;         // ring depth per wave
+constexpr int kTail1MaxTiles = 16; // tiles per workgroup (one staged weight-scale row each)
 
 __global__ __launch_bounds__(256) void draft_tail1_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ residual,
@@ -907,30 +913,37 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
     constexpr int SLOT = 2 * 64;             // one 16-row weight tile (uint4s)
     constexpr int PER_BLOCK = 2;
     constexpr int NSTEP = (kTail1MaxH + 2047) / 2048;
+    static_assert((D - 1) * PER_BLOCK <= 63, "vmcnt holds at most 63");
     __shared__ __align__(16) uint4 ring[4][D * SLOT];
+    // norm inputs as copied: per step k, hidden and residual in column order;
+    // the norm weight as two 1 KB halves per (step, wave): lane l's columns
+    // 8t..8t+3 in the first, 8t+4..8t+7 in the second
+    __shared__ __align__(16) uint4 h_lds[NSTEP * 256];
+    __shared__ __align__(16) uint4 r_lds[NSTEP * 256];
+    __shared__ __align__(16) uint4 g_lds[NSTEP * 2 * 256];
     __shared__ __align__(16) uint8_t a_lds[kTail1MaxH];
     __shared__ __align__(16) float sa_lds[kStreamMaxKB];
-    __shared__ __align__(16) float sw_lds[4][kStreamMaxKB];
+    __shared__ __align__(16) float sw_lds[kTail1MaxTiles][kStreamMaxKB];
+    __shared__ float part[2][4][16];
     __shared__ float wave_sum[4];
+    __shared__ unsigned long long red[256];
     __shared__ int last_flag;
-    // after the streams: wave w's partials in its own ring, the final
-    // reduction scratch in wave 0's (LDS is the occupancy limit: five
-    // workgroups per CU)
-    unsigned long long* red = reinterpret_cast<unsigned long long*>(&ring[0][0]);
-    auto part = [&](int w) { return reinterpret_cast<float*>(&ring[w][0]); };   // [4][64]
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int KB = H >> 7;
-    const int tile = xcd_contiguous((int)blockIdx.x, total_tiles);
-    const int n0 = tile * 16;
-    // this wave's K blocks [kb0, kb1), padded to whole rings
+    const int G = (int)gridDim.x;
+    const int b = (int)blockIdx.x;
+    const int ntiles = (total_tiles - b + G - 1) / G;   // this workgroup's tiles: b, b + G, ...
+    // this wave's K blocks of every tile [kb0, kb1); every wave walks NBU
+    // units per tile (units past its range are dead: zero factor)
     const int kb0 = (wave * KB) >> 2, kb1 = ((wave + 1) * KB) >> 2;
     const int nb = kb1 - kb0;
-    const int nbp = (nb + D - 1) / D * D;
+    const int NBU = (KB + 3) >> 2;
+    const int nunits = ntiles * NBU;
+    const int nup = (nunits + D - 1) / D * D;
 
-    const uint8_t* wbase = w_codes + (size_t)n0 * (size_t)H;
     uint32_t woff[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -941,46 +954,55 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
     const int fpos0 = fr * 8 + ring_pos(fr, fg);
     const int fpos1 = fr * 8 + ring_pos(fr, fg + 4);
     const uint32_t ring0 = lds_addr(&ring[wave][0]);
-    auto refill = [&](int j, int kb) {
-        const uint8_t* wb = wbase + (size_t)kb * kBlock;
+    // unit u: tile i = u / NBU, block slot j = u % NBU of this wave's range
+    // (clamped: units past the last request the last one again)
+    auto refill = [&](int slot, int u) {
+        const int uc = min(u, nunits - 1);
+        const int i = uc / NBU, j = uc - i * NBU;
+        const int kb = kb0 + min(j, nb - 1);
+        const uint8_t* wb = w_codes + (size_t)(b + i * G) * 16 * (size_t)H + (size_t)kb * kBlock;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) lds_copy16_stream(wb, woff[q], ring0 + (uint32_t)(j * SLOT + q * 64) * 16u);
+        for (int q = 0; q < 2; ++q) lds_copy16_stream(wb, woff[q], ring0 + (uint32_t)(slot * SLOT + q * 64) * 16u);
     };
 
-    // 1. the row's norm inputs (thread t owns columns k*2048 + 8t .. +7 of
-    //    each step): all loads issue before any use (clamped addresses,
-    //    zeroed values, no branch) and are waited for here, before any weight
-    //    copy is issued, so the wait does not include the ring (the counter
-    //    is in order: a load issued after the copies would complete only
-    //    after them, and the whole grid's first copies take microseconds to
-    //    drain from HBM)
-    uint4 hraw[NSTEP], rraw[NSTEP];
+    // 1. copies, oldest first: the norm inputs (thread t's 16-byte pieces of
+    //    columns k*2048 + 8t, clamped into the row), the weight-scale rows of
+    //    the workgroup's tiles (first and last tile's row span, lanes past KB
+    //    idle), then the first D-1 units of the ring
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+        const uint32_t cc = (uint32_t)min(k * 2048 + t * 8, H - 8);
+        const uint32_t dst = (uint32_t)(k * 256 + wave * 64) * 16u;
+        lds_copy16(reinterpret_cast<const uint8_t*>(hidden), cc * 2u, lds_addr(h_lds) + dst);
+        lds_copy16(reinterpret_cast<const uint8_t*>(residual), cc * 2u, lds_addr(r_lds) + dst);
+        lds_copy16(reinterpret_cast<const uint8_t*>(gamma), cc * 4u, lds_addr(g_lds) + (uint32_t)((k * 2 * 256) + wave * 64) * 16u);
+        lds_copy16(reinterpret_cast<const uint8_t*>(gamma), cc * 4u + 16u,
+                   lds_addr(g_lds) + (uint32_t)((k * 2 + 1) * 256 + wave * 64) * 16u);
+    }
+    // weight-scale rows: tile b + i*G lies in row ((b + i*G) * 16) >> 7;
+    // slot i holds tile i's row (the host keeps ntiles <= kTail1MaxTiles)
+    for (int i = wave; i < ntiles; i += 4)
+        lds_copy4(w_scales + (size_t)(((b + i * G) * 16) >> 7) * KB, (uint32_t)min(lane, KB - 1) * 4u,
+                  lds_addr(&sw_lds[0][0]) + (uint32_t)i * kStreamMaxKB * 4u);
+    int rq = 0;   // next unit to request
+#pragma unroll
+    for (int s2 = 0; s2 < D - 1; ++s2) refill(s2, rq++);
+
+    // 2. wait for this wave's norm copies only (the sw rows and the ring stay
+    //    in flight), then all waves' (barrier), then norm_quant_kernel's body
+    {
+        const int nsw = (ntiles - wave + 3) / 4;   // this wave's weight-scale copies
+        wait_vm(max(nsw, 0) + (D - 1) * PER_BLOCK);
+    }
+    __syncthreads();
+    float sv[NSTEP][8];
     float4 graw[NSTEP][2];
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k) {
-        const int cc = min(k * 2048 + t * 8, H - 8);
-        hraw[k] = *reinterpret_cast<const uint4*>(hidden + cc);
-        rraw[k] = *reinterpret_cast<const uint4*>(residual + cc);
-        graw[k][0] = *reinterpret_cast<const float4*>(gamma + cc);
-        graw[k][1] = *reinterpret_cast<const float4*>(gamma + cc + 4);
-    }
-    MTPD_WAIT_VM(0);
-    asm volatile("" ::: "memory");
-
-    // 2. per wave: the weight-scale row and the first D blocks of its range,
-    //    in flight while the norm runs
-    if (nb > 0) {
-        lds_copy4(w_scales + (size_t)(n0 >> 7) * KB, (uint32_t)min(lane, KB - 1) * 4u, lds_addr(&sw_lds[wave][0]));
-#pragma unroll
-        for (int j = 0; j < D; ++j) refill(j, kb0 + min(j, nb - 1));
-    }
-
-    // 3. norm_quant_kernel's body for the row; codes and scales go to LDS
-    float sv[NSTEP][8];
-#pragma unroll
-    for (int k = 0; k < NSTEP; ++k) {
         const float live = k * 2048 + t * 8 < H ? 1.f : 0.f;
-        const uint4 hv = hraw[k], rv = rraw[k];
+        const uint4 hv = h_lds[k * 256 + t], rv = r_lds[k * 256 + t];
+        graw[k][0] = *reinterpret_cast<const float4*>(&g_lds[(k * 2) * 256 + t]);
+        graw[k][1] = *reinterpret_cast<const float4*>(&g_lds[(k * 2 + 1) * 256 + t]);
         sv[k][0] = (bf16_lo(hv.x) + bf16_lo(rv.x)) * live;
         sv[k][1] = (bf16_hi(hv.x) + bf16_hi(rv.x)) * live;
         sv[k][2] = (bf16_lo(hv.y) + bf16_lo(rv.y)) * live;
@@ -1037,49 +1059,51 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
         *reinterpret_cast<uint2*>(&a_lds[c]) = make_uint2((uint32_t)lo, (uint32_t)hi);
         if ((t & 15) == 0) sa_lds[c >> 7] = scale;
     }
-    __syncthreads();   // also completes every wave's ring prologue
+    __syncthreads();
 
-    // 4. the weight stream over this wave's blocks; fragment rows all read
-    //    the packed row
+    // 3. the weight stream: every unit's fragment rows all read the packed
+    //    row; at each tile end the four partials meet in LDS (double-buffered
+    //    by tile parity) and wave 0 folds the tile's keys into its running best
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    const float* swv = &sw_lds[wave][0];
-    auto compute = [&](int j, int i) {   // i: block index inside the range
-        const int kb = kb0 + min(i, nb - 1);
-        const float f = sa_lds[kb] * (i < nb ? swv[kb] : 0.f);
+    uint64_t best = 0;
+    int ci = 0, cj = 0;   // unit being consumed: tile ci, slot cj
+    auto compute = [&](int slot) {
+        const bool live = ci < ntiles && cj < nb;
+        const int kb = kb0 + min(cj, nb - 1);
+        const float swv = sw_lds[min(ci, ntiles - 1)][kb];
+        const float f = sa_lds[kb] * (live ? swv : 0.f);
         const uint4 a0 = *reinterpret_cast<const uint4*>(&a_lds[kb * kBlock + fg * 16]);
         const uint4 a1 = *reinterpret_cast<const uint4*>(&a_lds[kb * kBlock + 64 + fg * 16]);
-        const uint4* tw = &ring[wave][j * SLOT];
+        const uint4* tw = &ring[wave][slot * SLOT];
         const v4f p = mfma_e4m3(make_frag(a0, a1), make_frag(tw[fpos0], tw[fpos1]));
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] = fmaf(p[r], f, acc[r]);
     };
-    if (nb > 0) {
-        int c = 0;
-        for (; c + D < nbp; c += D) {
-#pragma unroll
-            for (int j = 0; j < D; ++j) {
-                wait_vm((D - 1) * PER_BLOCK);
-                compute(j, c + j);
-                refill(j, kb0 + min(c + D + j, nb - 1));
-                __builtin_amdgcn_sched_barrier(0);
-            }
+    auto tile_end = [&]() {
+        float* pb = &part[ci & 1][0][0];
+        if (lane < 16) pb[wave * 16 + lane] = acc[0];
+        acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
+        __syncthreads();
+        if (wave == 0 && lane < 16) {
+            const float z = ((pb[lane] + pb[16 + lane]) + pb[32 + lane]) + pb[48 + lane];
+            best = u64_max(best, argmax_key(z, (uint32_t)((b + ci * G) * 16 + lane)));
         }
+    };
+    for (int c = 0; c < nup; c += D) {
 #pragma unroll
         for (int j = 0; j < D; ++j) {
-            wait_vm((D - 1 - j) * PER_BLOCK);
-            compute(j, c + j);
+            wait_vm((D - 2) * PER_BLOCK);
+            refill((j + D - 1) % D, rq++);
+            compute(j);
+            if (ci < ntiles && cj == NBU - 1) tile_end();
+            if (++cj == NBU) { cj = 0; ++ci; }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    MTPD_WAIT_VM(0);   // the clamped tail refills, before LDS is reused
 
-    // 5. partials meet in LDS, summed in wave order (row 0 sits in lanes
-    //    0..15, element 0)
-    if (wave > 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) part(wave)[r * 64 + lane] = acc[r];
-    }
-    // one workgroup stores the row's outputs (every copy has completed)
-    if (tile == 0) {
+    // 4. outputs of the row (workgroup 0), the row's best key, arrival
+    if (b == 0) {
 #pragma unroll
         for (int k = 0; k < NSTEP; ++k) {
             const int c = k * 2048 + t * 8;
@@ -1090,16 +1114,13 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
         }
         if (t < KB) scales[t] = sa_lds[t];
     }
-    __syncthreads();
     if (wave == 0) {
-        const float z = ((acc[0] + part(1)[lane]) + part(2)[lane]) + part(3)[lane];
-        uint64_t best = argmax_key(z, (uint32_t)(n0 + (lane & 15)));
 #pragma unroll
         for (int off = 8; off > 0; off >>= 1) best = u64_max(best, shfl_xor_u64(best, off));
         uint64_t old = 0;
-        if (lane == 0) old = merge_key(ws, 1, tile, 0, best);
+        if (lane == 0) old = merge_key(ws, 1, b, 0, best);
         const unsigned int dep = __builtin_amdgcn_ballot_w64(never_nonzero(old) != 0) != 0 ? 1u : 0u;
-        if (lane == 0) last_flag = arrive(ws, tile, total_tiles, dep) ? 1 : 0;
+        if (lane == 0) last_flag = arrive(ws, b, G, dep) ? 1 : 0;
     }
     __syncthreads();
     if (!last_flag) return;
@@ -1112,15 +1133,22 @@ bool use_draft_tail1(int64_t M, int64_t H) {
     return M == 1 && H <= kTail1MaxH;
 }
 
+int64_t draft_tail1_grid(int64_t V) {
+    // one resident workgroup per CU, at most kTail1MaxTiles tiles each
+    const int64_t tiles = V / 16;
+    return std::max<int64_t>(std::min<int64_t>(tiles, device_cus()), (tiles + kTail1MaxTiles - 1) / kTail1MaxTiles);
+}
+
 hipError_t launch_draft_tail1(const uint16_t* hidden, const uint16_t* residual, const float* gamma, float eps,
                               int64_t H, const uint8_t* w_codes, const float* w_scales, int64_t V,
                               uint16_t* out_hidden, uint8_t* codes, float* scales, float* out_max, int32_t* out_idx,
                               void* workspace, hipStream_t stream) {
     const int64_t tiles = V / 16;
     if (tiles > 0x7FFFFFFF || H > kTail1MaxH) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(draft_tail1_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, hidden, residual,
-                       gamma, eps, (int)H, w_codes, w_scales, (int)tiles, out_hidden, codes, scales, out_max,
-                       out_idx, argmax_ws(workspace, 1));
+    const int64_t grid = draft_tail1_grid(V);
+    hipLaunchKernelGGL(draft_tail1_kernel, dim3((unsigned)grid), dim3(256), 0, stream, hidden, residual, gamma, eps,
+                       (int)H, w_codes, w_scales, (int)tiles, out_hidden, codes, scales, out_max, out_idx,
+                       argmax_ws(workspace, 1));
     return hipGetLastError();
 }
 

@@ -151,7 +151,8 @@ const char* mtpd_draft_tail_plan(int64_t M, int64_t V, int64_t H) {
         V > kMaxV || V % mtpd::kBlock)
         return buf;
     if (mtpd::use_draft_tail1(M, H)) {
-        snprintf(buf, sizeof buf, "draft_tail1_kernel grid=%lldx256", (long long)(V / 16));
+        snprintf(buf, sizeof buf, "draft_tail1_kernel grid=%lldx256 (%lld tiles)", (long long)mtpd::draft_tail1_grid(V),
+                 (long long)(V / 16));
         return buf;
     }
     char lm[160];
