@@ -899,7 +899,7 @@ hipError_t launch_lmhead_topk(const LmheadArgs& a, int k, float* out_val, int32_
 // ---------------------------------------------------------------------------
 
 constexpr int kTail1MaxH = 6144;   // NSTEP <= 3 steps of 2048 columns
-constexpr int kTail1D = 8;         // ring depth per wave
+constexpr int kTail1D = 6;         // ring depth per wave
 constexpr int kTail1MaxTiles = 16; // tiles per workgroup (one staged weight-scale row each)
 
 __global__ __launch_bounds__(256) void draft_tail1_kernel(
