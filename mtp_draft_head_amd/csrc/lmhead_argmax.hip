@@ -424,7 +424,7 @@ bool use_rows(int64_t n_rows, int64_t V, int64_t H, int64_t a_rows, RowsTile* ou
         if (sscanf(e, "%d,%d,%d", &o.nt, &o.nw, &o.d) == 3) cand[nc++] = o;
     }
     if (mt == 4) {
-        cand[nc++] = {4, 2, 4, 3};
+        cand[nc++] = {4, 2, 4, 5};
         cand[nc++] = {4, 1, 4, 6};
     } else {
         cand[nc++] = {2, 2, 4, 4};

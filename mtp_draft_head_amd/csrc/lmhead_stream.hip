@@ -190,7 +190,22 @@ __global__ __launch_bounds__(64) void lmhead_stream_kernel(
         for (int i = 0; i < 4; ++i) acc[nt][i] = 0.f;
 
     // scale reads: rows 4 * fg + i of block kb; padding blocks (kb >= KB) get
-    // a zero factor
+    // a zero factor.  Each block's partials are promoted one block late (pp,
+    // pf), so the FMAs never wait for the MFMA just issued; the order of the
+    // sum is unchanged.
+    v4f pp[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) pp[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+    float4 pf = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto promote = [&]() {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            acc[nt][0] = fmaf(pp[nt][0], pf.x, acc[nt][0]);
+            acc[nt][1] = fmaf(pp[nt][1], pf.y, acc[nt][1]);
+            acc[nt][2] = fmaf(pp[nt][2], pf.z, acc[nt][2]);
+            acc[nt][3] = fmaf(pp[nt][3], pf.w, acc[nt][3]);
+        }
+    };
     auto compute = [&](int j, int kb) {
         const int kc = min(kb, kStreamMaxKB - 1);
         const float swl = sw_lds[kc];
@@ -199,15 +214,16 @@ __global__ __launch_bounds__(64) void lmhead_stream_kernel(
         const float4 f = make_float4(sa4.x * sw, sa4.y * sw, sa4.z * sw, sa4.w * sw);
         const uint4* ta = &ring[j * SLOT + NT * 128];
         const v8i af = make_frag(ta[apos0], ta[apos1]);
+        v4f p[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const uint4* tw = &ring[j * SLOT + nt * 128];
-            const v4f p = mfma_e4m3(af, make_frag(tw[fpos0], tw[fpos1]));
-            acc[nt][0] = fmaf(p[0], f.x, acc[nt][0]);
-            acc[nt][1] = fmaf(p[1], f.y, acc[nt][1]);
-            acc[nt][2] = fmaf(p[2], f.z, acc[nt][2]);
-            acc[nt][3] = fmaf(p[3], f.w, acc[nt][3]);
+            p[nt] = mfma_e4m3(af, make_frag(tw[fpos0], tw[fpos1]));
         }
+        promote();
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) pp[nt] = p[nt];
+        pf = f;
     };
 
     // prologue: the activation scales of the 16 fragment rows, loaded into
@@ -254,6 +270,7 @@ __global__ __launch_bounds__(64) void lmhead_stream_kernel(
         compute(j, c + j);
         __builtin_amdgcn_sched_barrier(0);
     }
+    promote();   // the last block's partials
 
     // per activation row (4 * (lane / 16) + i) the best key over the wave's
     // NT * 16 vocab rows
@@ -548,6 +565,33 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
         run1[s2] = 0;
     }
 
+    // each unit's partials are promoted one unit late (pp, pf): the FMAs of
+    // unit u run beside the MFMAs of unit u + 1 instead of waiting for fresh
+    // results; the order of every sum is unchanged
+    v4f pp[MT][NT];
+    float4 pf[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        pf[mt] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) pp[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    auto promote = [&](int mt) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            acc[mt][nt][0] = fmaf(pp[mt][nt][0], pf[mt].x, acc[mt][nt][0]);
+            acc[mt][nt][1] = fmaf(pp[mt][nt][1], pf[mt].y, acc[mt][nt][1]);
+            acc[mt][nt][2] = fmaf(pp[mt][nt][2], pf[mt].z, acc[mt][nt][2]);
+            acc[mt][nt][3] = fmaf(pp[mt][nt][3], pf[mt].w, acc[mt][nt][3]);
+        }
+    };
+    auto flush = [&]() {   // promote the pending unit and clear it
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            promote(mt);
+            pf[mt] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
     auto compute = [&](int j, int i, int kb, bool live) {
         const float swl = sw_lds[i][kb];
         const float sw = live ? swl : 0.f;
@@ -560,21 +604,20 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
             const uint4* ta = &aring[j * ASLOT + mt * 128];
             const v8i af = make_frag(ta[fpos0], ta[fpos1]);
             const float4 sa4 = *reinterpret_cast<const float4*>(&sa_lds[kb * ROWS + mt * 16 + 4 * fg]);
-            const float f0 = sa4.x * sw, f1 = sa4.y * sw, f2 = sa4.z * sw, f3 = sa4.w * sw;
+            v4f p[NT];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const v4f p = mfma_e4m3(af, bf[nt]);
-                acc[mt][nt][0] = fmaf(p[0], f0, acc[mt][nt][0]);
-                acc[mt][nt][1] = fmaf(p[1], f1, acc[mt][nt][1]);
-                acc[mt][nt][2] = fmaf(p[2], f2, acc[mt][nt][2]);
-                acc[mt][nt][3] = fmaf(p[3], f3, acc[mt][nt][3]);
-            }
+            for (int nt = 0; nt < NT; ++nt) p[nt] = mfma_e4m3(af, bf[nt]);
+            promote(mt);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) pp[mt][nt] = p[nt];
+            pf[mt] = make_float4(sa4.x * sw, sa4.y * sw, sa4.z * sw, sa4.w * sw);
         }
     };
     // a finished tile: per-row best over this wave's columns, folded into the
     // wave's running maxima (top-k mode: the wave's best k per row, written
     // to its list); the accumulators restart
     auto fold = [&](int i) {
+        flush();   // the tile's last unit
         const int n0 = (b + i * G) * TROWS + wave * NT * 16;
         if constexpr (TOPK) {
             const int j = lane & 15;
@@ -1067,6 +1110,10 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     uint64_t best = 0;
     int ci = 0, cj = 0;   // unit being consumed: tile ci, slot cj
+    // each unit's partial is promoted one unit late (pp, pf), beside the
+    // next unit's MFMA; the order of the sum is unchanged
+    v4f pp = v4f{0.f, 0.f, 0.f, 0.f};
+    float pf = 0.f;
     auto compute = [&](int slot) {
         const bool live = ci < ntiles && cj < nb;
         const int kb = kb0 + min(cj, nb - 1);
@@ -1077,9 +1124,14 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
         const uint4* tw = &ring[wave][slot * SLOT];
         const v4f p = mfma_e4m3(make_frag(a0, a1), make_frag(tw[fpos0], tw[fpos1]));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = fmaf(p[r], f, acc[r]);
+        for (int r = 0; r < 4; ++r) acc[r] = fmaf(pp[r], pf, acc[r]);
+        pp = p;
+        pf = f;
     };
     auto tile_end = [&]() {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = fmaf(pp[r], pf, acc[r]);   // the tile's last unit
+        pf = 0.f;
         float* pb = &part[ci & 1][0][0];
         if (lane < 16) pb[wave * 16 + lane] = acc[0];
         acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
