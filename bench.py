@@ -115,8 +115,9 @@ TOPK_K = 8        # k of the topk variant (--topk)
 
 
 def topk_list_bytes(M, V, k) -> int:
-    """Candidate-list bytes one top-k pass writes (and its merge reads once)."""
-    return M * (V // 32) * k * 8
+    """Candidate-list bytes one top-k pass writes: k keys per row for each of
+    the 4 waves of every workgroup (one per CU, at most one per 128-row tile)."""
+    return M * min(V // 128, 256) * 4 * k * 8
 
 
 def allreduce_norm_bytes(P, M, H) -> int:
