@@ -32,6 +32,50 @@ __device__ __forceinline__ int cvt_e4m3x2(float x, float y, int old) {
     return __builtin_amdgcn_cvt_pk_fp8_f32(x, y, old, HIGH);
 }
 
+// Eight fp32 values -> eight bf16 (round to nearest even), in column order.
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&y)[8]) {
+    uint4 hb;
+    hb.x = bf16_rne(y[0]) | (bf16_rne(y[1]) << 16);
+    hb.y = bf16_rne(y[2]) | (bf16_rne(y[3]) << 16);
+    hb.z = bf16_rne(y[4]) | (bf16_rne(y[5]) << 16);
+    hb.w = bf16_rne(y[6]) | (bf16_rne(y[7]) << 16);
+    return hb;
+}
+
+// E4M3 codes of eight values of one 128-column block whose scale is
+// scale = RN_f32(amax / 448): code = E4M3(RN_f32(y / scale)) saturated to
+// +-448, ties to even, a zero quotient keeping the sign of y; a zero scale
+// gives +0 codes.  For scale in [2^-60, 2^60] the quotient comes from one
+// correctly rounded reciprocal r = RN(1/scale) per block: q0 = RN(y r), the
+// exact remainder e = y - scale q0 (one fma), and RN(q0 + e r), which is the
+// correctly rounded quotient by Markstein's theorem (r within half an ulp of
+// 1/scale, q0 within one ulp of the quotient; the range keeps r, q0 and e
+// clear of overflow and underflow wherever the quotient reaches the E4M3
+// range).  Three operations per value instead of a full division.
+__device__ __forceinline__ uint2 quant_e4m3x8(const float (&y)[8], float scale) {
+    float q[8];
+    if (scale >= 0x1p-60f && scale <= 0x1p60f) {
+        const float r = 1.0f / scale;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float q0 = y[i] * r;
+            const float e = fmaf(-scale, q0, y[i]);
+            q[i] = copysignf(fmaf(e, r, q0), y[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = scale > 0.f ? y[i] / scale : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_fmed3f(q[i], -448.f, 448.f);
+    int lo = 0, hi = 0;
+    lo = cvt_e4m3x2<false>(q[0], q[1], lo);
+    lo = cvt_e4m3x2<true>(q[2], q[3], lo);
+    hi = cvt_e4m3x2<false>(q[4], q[5], hi);
+    hi = cvt_e4m3x2<true>(q[6], q[7], hi);
+    return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
 // Order-preserving map of an fp32 logit to u32 (-0 folded onto +0), packed
 // with the vocab index so that the u64 maximum is the largest logit and,
 // among equal logits, the lowest index.
@@ -60,6 +104,43 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
     lo = __shfl_xor(lo, mask);
     hi = __shfl_xor(hi, mask);
     return ((uint64_t)hi << 32) | lo;
+}
+
+// DPP moves inside each 16-lane row (gfx9 dpp_ctrl encodings): 0xB1 quad_perm
+// [1,0,3,2] (lane ^ 1), 0x4E quad_perm [2,3,0,1] (lane ^ 2), 0x141
+// row_half_mirror (lane i of each 8-lane half takes lane 7 - i), 0x140
+// row_mirror (lane i takes lane 15 - i).  Each is one VALU operand modifier
+// instead of an LDS round trip, and never reads outside the row, so a row
+// that is entirely active gives the same result whatever the other rows do.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over each 16-lane row, in every lane of the row (exact in any
+// order).
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    return fmaxf(v, dpp_f32<0x140>(v));
+}
+
+// Sum over the 64 lanes of a fully active wave with one fixed association:
+// lane pairs, then quads, then the two quads of each half-row, the two halves
+// of each row (each step adds two partial sums of the same lanes, so the
+// lanes of a group agree: fp addition commutes), and the four row sums as
+// (r0 + r1) + (r2 + r3).  Wave-uniform result.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v += dpp_f32<0xB1>(v);
+    v += dpp_f32<0x4E>(v);
+    v += dpp_f32<0x141>(v);
+    v += dpp_f32<0x140>(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // The dispatcher places workgroup b on XCD (b mod 8).  Give each XCD a

@@ -931,7 +931,7 @@ hipError_t launch_lmhead_topk(const LmheadArgs& a, int k, float* out_val, int32_
 //
 // Before the stream the workgroup computes the row's residual add + RMSNorm
 // + E4M3 packing itself (norm_quant_kernel's body for one row, thread for
-// thread: same per-thread fma order, same butterfly, same fixed-order sum of
+// thread: same per-thread fma order, same wave sum, same fixed-order sum of
 // the four wave totals), so the packed row and the bf16 hidden are
 // bit-identical to the two-kernel path; the packed row stays in LDS as the
 // MFMA activation (every fragment row reads row 0).  The norm inputs (bf16
@@ -1060,8 +1060,7 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
     for (int k = 0; k < NSTEP; ++k)
 #pragma unroll
         for (int i = 0; i < 8; ++i) ss = fmaf(sv[k][i], sv[k][i], ss);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    ss = wave_sum_f32(ss);
     if (lane == 0) wave_sum[wave] = ss;
     __syncthreads();
     const float total = (wave_sum[0] + wave_sum[1]) + (wave_sum[2] + wave_sum[3]);
@@ -1081,25 +1080,10 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
             y[i] = (sv[k][i] * rstd) * g[i];
             amax = fmaxf(amax, fabsf(y[i]));
         }
-        hb[k].x = bf16_rne(y[0]) | (bf16_rne(y[1]) << 16);
-        hb[k].y = bf16_rne(y[2]) | (bf16_rne(y[3]) << 16);
-        hb[k].z = bf16_rne(y[4]) | (bf16_rne(y[5]) << 16);
-        hb[k].w = bf16_rne(y[6]) | (bf16_rne(y[7]) << 16);
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        if (b == 0) hb[k] = pack_bf16x8(y);   // only workgroup 0 stores the recycled hidden
+        amax = row16_max(amax);
         const float scale = (float)((double)amax / 448.0);
-        float q[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float v = scale > 0.f ? y[i] / scale : 0.f;
-            q[i] = fminf(fmaxf(v, -448.f), 448.f);
-        }
-        int lo = 0, hi = 0;
-        lo = cvt_e4m3x2<false>(q[0], q[1], lo);
-        lo = cvt_e4m3x2<true>(q[2], q[3], lo);
-        hi = cvt_e4m3x2<false>(q[4], q[5], hi);
-        hi = cvt_e4m3x2<true>(q[6], q[7], hi);
-        *reinterpret_cast<uint2*>(&a_lds[c]) = make_uint2((uint32_t)lo, (uint32_t)hi);
+        *reinterpret_cast<uint2*>(&a_lds[c]) = quant_e4m3x8(y, scale);
         if ((t & 15) == 0) sa_lds[c >> 7] = scale;
     }
     __syncthreads();

@@ -11,10 +11,12 @@
 // bf16 vector from hidden and one from residual, and kept in registers (at
 // most 8 steps, H <= 16384).  Sixteen consecutive threads cover exactly one
 // 128-column scale block, so the block amax is a 16-lane shuffle reduction
-// and the block scale is known to all 16 lanes without LDS.  The row's sum
-// of squares is a per-thread fp32 sum, a 64-lane butterfly, and a fixed-order
-// sum of the four wave totals through LDS, so every thread sees the same
-// value and the result does not depend on scheduling.
+// and the block scale is known to all 16 lanes without LDS (DPP moves inside
+// the lane row).  The row's sum of squares is a per-thread fp32 sum, a wave
+// sum with one fixed association (DPP inside each 16-lane row, then the four
+// row sums), and a fixed-order sum of the four wave totals through LDS, so
+// every thread sees the same value and the result does not depend on
+// scheduling.
 //
 // Bytes per row: 4H read (hidden + residual) + 4H read of the norm weight
 // (cache-resident across rows) + 2H (bf16) + H (codes) + H/32 (scales)
@@ -42,8 +44,7 @@ __device__ __forceinline__ void norm_quant_finish(const float (&s)[NSTEP][8], co
     for (int k = 0; k < NSTEP; ++k)
 #pragma unroll
         for (int i = 0; i < 8; ++i) ss = fmaf(s[k][i], s[k][i], ss);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    ss = wave_sum_f32(ss);
     if ((t & 63) == 0) wave_sum[t >> 6] = ss;
     __syncthreads();
     const float total = (wave_sum[0] + wave_sum[1]) + (wave_sum[2] + wave_sum[3]);
@@ -63,30 +64,12 @@ __device__ __forceinline__ void norm_quant_finish(const float (&s)[NSTEP][8], co
             y[i] = (s[k][i] * rstd) * g[i];
             amax = fmaxf(amax, fabsf(y[i]));
         }
-        uint4 hb;
-        hb.x = bf16_rne(y[0]) | (bf16_rne(y[1]) << 16);
-        hb.y = bf16_rne(y[2]) | (bf16_rne(y[3]) << 16);
-        hb.z = bf16_rne(y[4]) | (bf16_rne(y[5]) << 16);
-        hb.w = bf16_rne(y[6]) | (bf16_rne(y[7]) << 16);
-        *reinterpret_cast<uint4*>(out_hidden + base + c) = hb;
-
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        *reinterpret_cast<uint4*>(out_hidden + base + c) = pack_bf16x8(y);
+        amax = row16_max(amax);
         // RN_f32(amax / 448): the fp64 quotient rounds once more to fp32; a
         // quotient by 448 = 7 * 64 never lands on a false fp32 halfway point.
         const float scale = (float)((double)amax / 448.0);
-        float q[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float v = scale > 0.f ? y[i] / scale : 0.f;   // correctly rounded fp32 quotient
-            q[i] = fminf(fmaxf(v, -448.f), 448.f);
-        }
-        int lo = 0, hi = 0;
-        lo = cvt_e4m3x2<false>(q[0], q[1], lo);
-        lo = cvt_e4m3x2<true>(q[2], q[3], lo);
-        hi = cvt_e4m3x2<false>(q[4], q[5], hi);
-        hi = cvt_e4m3x2<true>(q[6], q[7], hi);
-        *reinterpret_cast<uint2*>(codes + base + c) = make_uint2((uint32_t)lo, (uint32_t)hi);
+        *reinterpret_cast<uint2*>(codes + base + c) = quant_e4m3x8(y, scale);
         if ((t & 15) == 0) scales[row * KB + (c >> 7)] = scale;
     }
 }

@@ -272,6 +272,47 @@ def test_fused_one_row_draft_tail_matches_split(H, V, monkeypatch):
     check_lmhead(split[1], split[2], d, split[3], split[4])
 
 
+def _scaled_case(seed, M, H, V, row_mag, small_blocks=()):
+    """random_case with row m of hidden and residual scaled by row_mag[m], and
+    the listed (row, 128-column block) pairs 1e-30 times smaller still."""
+    d = inputs.random_case(seed, M, H, V)
+    for key in ("hidden", "residual"):
+        x = torch.from_numpy(d[key].view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+        x *= np.asarray(row_mag, np.float32)[:, None]
+        for m, kb in small_blocks:
+            x[m, kb * 128:(kb + 1) * 128] *= np.float32(1e-30)
+        d[key] = inputs.to_bf16_bits(x)
+    return d
+
+
+def test_block_scales_across_the_exponent_range(monkeypatch):
+    """Block scales from about 2^-107 to 2^-6: a row so small that eps
+    dominates its norm (scales below 2^-60, where the packing divides in full
+    rather than through the block's reciprocal), rows just above that, and a
+    normal row with blocks 1e-30 times smaller than the rest.  Hidden, codes
+    and scales against the oracle, the packing self-consistent, and every row
+    through the fused one-row tail bit for bit equal to the two-launch path."""
+    M, H, V = 4, 1024, 512
+    d = _scaled_case(31, M, H, V, [1e-20, 3e-18, 1e-16, 1.0], small_blocks=[(3, 1), (3, 5)])
+    h, r, g, wc, ws = to_dev(d)
+    out = mtpd.draft_tail(h, r, g, d["eps"], wc, ws)
+    r1, r2, r3 = check_norm_quant(d, *out[:3])
+    s = host(out[2])
+    say(f"  scales {s[s > 0].min():.3e} .. {s.max():.3e}; bf16 {r1}  codes {r2}")
+    assert s.min() > 0 and s.min() < 2.0 ** -100 and s[0].max() < 2.0 ** -60 and s[1].min() > 2.0 ** -60
+    check_self_consistent(out[1], out[2])
+    check_lmhead(out[1], out[2], d, out[3], out[4])
+    for m in range(M):
+        fused = mtpd.draft_tail(h[m:m + 1], r[m:m + 1], g, d["eps"], wc, ws)
+        monkeypatch.setenv("MTPD_DRAFT_TAIL", "split")
+        split = mtpd.draft_tail(h[m:m + 1], r[m:m + 1], g, d["eps"], wc, ws)
+        monkeypatch.delenv("MTPD_DRAFT_TAIL")
+        torch.cuda.synchronize()
+        for x, y in zip(fused[:3], split[:3]):
+            assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.uint8) if y.dtype == torch.bfloat16 else y), m
+
+
 @pytest.mark.parametrize("kernel", ["generic", "default"])
 def test_many_rows_both_kernels(kernel, monkeypatch):
     """More than 64 rows: the LDS-tiled 256x256 kernel by default, the generic
