@@ -42,40 +42,6 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&y)[8]) {
     return hb;
 }
 
-// E4M3 codes of eight values of one 128-column block whose scale is
-// scale = RN_f32(amax / 448): code = E4M3(RN_f32(y / scale)) saturated to
-// +-448, ties to even, a zero quotient keeping the sign of y; a zero scale
-// gives +0 codes.  For scale in [2^-60, 2^60] the quotient comes from one
-// correctly rounded reciprocal r = RN(1/scale) per block: q0 = RN(y r), the
-// exact remainder e = y - scale q0 (one fma), and RN(q0 + e r), which is the
-// correctly rounded quotient by Markstein's theorem (r within half an ulp of
-// 1/scale, q0 within one ulp of the quotient; the range keeps r, q0 and e
-// clear of overflow and underflow wherever the quotient reaches the E4M3
-// range).  Three operations per value instead of a full division.
-__device__ __forceinline__ uint2 quant_e4m3x8(const float (&y)[8], float scale) {
-    float q[8];
-    if (scale >= 0x1p-60f && scale <= 0x1p60f) {
-        const float r = 1.0f / scale;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float q0 = y[i] * r;
-            const float e = fmaf(-scale, q0, y[i]);
-            q[i] = copysignf(fmaf(e, r, q0), y[i]);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = scale > 0.f ? y[i] / scale : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_fmed3f(q[i], -448.f, 448.f);
-    int lo = 0, hi = 0;
-    lo = cvt_e4m3x2<false>(q[0], q[1], lo);
-    lo = cvt_e4m3x2<true>(q[2], q[3], lo);
-    hi = cvt_e4m3x2<false>(q[4], q[5], hi);
-    hi = cvt_e4m3x2<true>(q[6], q[7], hi);
-    return make_uint2((uint32_t)lo, (uint32_t)hi);
-}
-
 // Order-preserving map of an fp32 logit to u32 (-0 folded onto +0), packed
 // with the vocab index so that the u64 maximum is the largest logit and,
 // among equal logits, the lowest index.
@@ -141,6 +107,79 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
     const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
     const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
     return (r0 + r1) + (r2 + r3);
+}
+
+// E4M3 codes of eight values of one 128-column block whose scale is
+// scale = RN_f32(amax / 448): code = E4M3(RN_f32(y / scale)) saturated to
+// +-448, ties to even, a zero quotient keeping the sign of y; a zero scale
+// gives +0 codes.
+//
+// For scale in [2^-60, 2^60] the quotient comes from one correctly rounded
+// reciprocal r = RN(1/scale) per block: q0 = RN(y r), the exact remainder
+// e = y - scale q0 (one fma), and RN(q0 + e r), which is the correctly
+// rounded quotient by Markstein's theorem (r within half an ulp of 1/scale,
+// q0 within one ulp of the quotient; the range keeps r, q0 and e clear of
+// overflow and underflow wherever the quotient reaches the E4M3 range).
+// Three operations per value instead of a full division; other scales take
+// the full division.
+__device__ __forceinline__ bool quant_fast_range(float scale) { return scale >= 0x1p-60f && scale <= 0x1p60f; }
+
+__device__ __forceinline__ uint2 pack_e4m3x8(float (&q)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_fmed3f(q[i], -448.f, 448.f);
+    int lo = 0, hi = 0;
+    lo = cvt_e4m3x2<false>(q[0], q[1], lo);
+    lo = cvt_e4m3x2<true>(q[2], q[3], lo);
+    hi = cvt_e4m3x2<false>(q[4], q[5], hi);
+    hi = cvt_e4m3x2<true>(q[6], q[7], hi);
+    return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+// quant_fast_range(scale) must hold
+__device__ __forceinline__ uint2 quant_e4m3x8_fast(const float (&y)[8], float scale) {
+    const float r = 1.0f / scale;
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float q0 = y[i] * r;
+        const float e = fmaf(-scale, q0, y[i]);
+        q[i] = copysignf(fmaf(e, r, q0), y[i]);
+    }
+    return pack_e4m3x8(q);
+}
+
+__device__ __forceinline__ uint2 quant_e4m3x8_div(const float (&y)[8], float scale) {
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = scale > 0.f ? y[i] / scale : 0.f;
+    return pack_e4m3x8(q);
+}
+
+// One thread's share of a row's packing: NSTEP groups of 8 columns, each
+// inside one 128-column block whose 16 lanes form a DPP row.  Per group: the
+// block amax (row16_max), scale = RN_f32(amax / 448) (the fp64 quotient
+// rounds once more to fp32; a quotient by 448 = 7 * 64 never lands on a false
+// fp32 halfway point), and the codes.  Straight-line over the groups (the
+// rare full divisions come after), so their latency chains interleave.
+template <int NSTEP>
+__device__ __forceinline__ void quant_groups(const float (&y)[NSTEP][8], float (&scale)[NSTEP],
+                                             uint2 (&code)[NSTEP]) {
+    bool slow = false;
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[k][i]));
+        amax = row16_max(amax);
+        scale[k] = (float)((double)amax / 448.0);
+        code[k] = quant_e4m3x8_fast(y[k], scale[k]);
+        slow |= !quant_fast_range(scale[k]);
+    }
+    if (slow) {
+#pragma unroll
+        for (int k = 0; k < NSTEP; ++k)
+            if (!quant_fast_range(scale[k])) code[k] = quant_e4m3x8_div(y[k], scale[k]);
+    }
 }
 
 // The dispatcher places workgroup b on XCD (b mod 8).  Give each XCD a

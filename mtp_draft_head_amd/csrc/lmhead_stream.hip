@@ -1066,25 +1066,25 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
     const float total = (wave_sum[0] + wave_sum[1]) + (wave_sum[2] + wave_sum[3]);
     const float rstd = (float)(1.0 / sqrt((double)total / (double)H + (double)eps));
 
-    uint4 hb[NSTEP];
+    // every group computed (columns past H hold s = 0; they fill whole
+    // 128-column blocks, which are not stored)
+    float y[NSTEP][8];
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+        const float4 g0 = graw[k][0], g1 = graw[k][1];
+        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[k][i] = (sv[k][i] * rstd) * g[i];
+    }
+    float bscale[NSTEP];
+    uint2 code[NSTEP];
+    quant_groups<NSTEP>(y, bscale, code);
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k) {
         const int c = k * 2048 + t * 8;
         if (c >= H) continue;   // uniform over each 16-thread scale block
-        const float4 g0 = graw[k][0], g1 = graw[k][1];
-        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        float y[8];
-        float amax = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            y[i] = (sv[k][i] * rstd) * g[i];
-            amax = fmaxf(amax, fabsf(y[i]));
-        }
-        if (b == 0) hb[k] = pack_bf16x8(y);   // only workgroup 0 stores the recycled hidden
-        amax = row16_max(amax);
-        const float scale = (float)((double)amax / 448.0);
-        *reinterpret_cast<uint2*>(&a_lds[c]) = quant_e4m3x8(y, scale);
-        if ((t & 15) == 0) sa_lds[c >> 7] = scale;
+        *reinterpret_cast<uint2*>(&a_lds[c]) = code[k];
+        if ((t & 15) == 0) sa_lds[c >> 7] = bscale[k];
     }
     __syncthreads();
 
@@ -1144,7 +1144,7 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
         for (int k = 0; k < NSTEP; ++k) {
             const int c = k * 2048 + t * 8;
             if (c < H) {
-                *reinterpret_cast<uint4*>(out_hidden + c) = hb[k];
+                *reinterpret_cast<uint4*>(out_hidden + c) = pack_bf16x8(y[k]);
                 *reinterpret_cast<uint2*>(codes + c) = *reinterpret_cast<const uint2*>(&a_lds[c]);
             }
         }

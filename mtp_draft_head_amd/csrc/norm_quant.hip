@@ -50,27 +50,28 @@ __device__ __forceinline__ void norm_quant_finish(const float (&s)[NSTEP][8], co
     const float total = (wave_sum[0] + wave_sum[1]) + (wave_sum[2] + wave_sum[3]);
     const float rstd = (float)(1.0 / sqrt((double)total / (double)H + (double)eps));
 
+    // every group computed (columns past H hold s = 0 and read a clamped
+    // norm weight; they fill whole 128-column blocks, which are not stored)
+    float y[NSTEP][8];
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+        const int c = min(k * 2048 + t * 8, H - 8);
+        const float4 g0 = *reinterpret_cast<const float4*>(gamma + c);
+        const float4 g1 = *reinterpret_cast<const float4*>(gamma + c + 4);
+        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[k][i] = (s[k][i] * rstd) * g[i];
+    }
+    float scale[NSTEP];
+    uint2 code[NSTEP];
+    quant_groups<NSTEP>(y, scale, code);
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k) {
         const int c = k * 2048 + t * 8;
         if (c >= H) continue;   // uniform over each 16-thread scale block
-        const float4 g0 = *reinterpret_cast<const float4*>(gamma + c);
-        const float4 g1 = *reinterpret_cast<const float4*>(gamma + c + 4);
-        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        float y[8];
-        float amax = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            y[i] = (s[k][i] * rstd) * g[i];
-            amax = fmaxf(amax, fabsf(y[i]));
-        }
-        *reinterpret_cast<uint4*>(out_hidden + base + c) = pack_bf16x8(y);
-        amax = row16_max(amax);
-        // RN_f32(amax / 448): the fp64 quotient rounds once more to fp32; a
-        // quotient by 448 = 7 * 64 never lands on a false fp32 halfway point.
-        const float scale = (float)((double)amax / 448.0);
-        *reinterpret_cast<uint2*>(codes + base + c) = quant_e4m3x8(y, scale);
-        if ((t & 15) == 0) scales[row * KB + (c >> 7)] = scale;
+        *reinterpret_cast<uint4*>(out_hidden + base + c) = pack_bf16x8(y[k]);
+        *reinterpret_cast<uint2*>(codes + base + c) = code[k];
+        if ((t & 15) == 0) scales[row * KB + (c >> 7)] = scale[k];
     }
 }
 
