@@ -96,6 +96,15 @@ __device__ __forceinline__ bool arrive(const ArgmaxWs& ws, int tile, int total_t
     return prev2 == groups - 1;
 }
 
+// The same with one counter for the whole launch: one round trip fewer, but
+// every arrival queues on one line, so for grids of a few hundred
+// workgroups whose arrivals spread out in time.
+__device__ __forceinline__ bool arrive_flat(const ArgmaxWs& ws, int total, unsigned int dep) {
+    const unsigned int prev = __hip_atomic_fetch_add(&ws.counters[kArriveGroups * kCounterStride], 1u + dep,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return prev == (unsigned int)total - 1;
+}
+
 // The last workgroup (all NTHREADS threads): reduce the P partitions of every
 // row, decode (max, index), and leave keys and counters zero.  red: LDS
 // scratch of NTHREADS u64.

@@ -1156,7 +1156,7 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
         uint64_t old = 0;
         if (lane == 0) old = merge_key(ws, 1, b, 0, best);
         const unsigned int dep = __builtin_amdgcn_ballot_w64(never_nonzero(old) != 0) != 0 ? 1u : 0u;
-        if (lane == 0) last_flag = arrive(ws, b, G, dep) ? 1 : 0;
+        if (lane == 0) last_flag = arrive_flat(ws, G, dep) ? 1 : 0;
     }
     __syncthreads();
     if (!last_flag) return;

@@ -253,11 +253,15 @@ def test_stream_rows_kernel_vocab_shard_shape(workloads):
                                                                           d["w_scales"][:S // 128], rows=[k])[0])))
 
 
-@pytest.mark.parametrize("H,V", [(128, 256), (1152, 2048), (2304, 4096), (6144, 18944)])
+# 16-row tiles per workgroup: one (256, 2048, 4096), one or two (5120), four
+# or five (18944), eight or nine (33152), sixteen on 592 workgroups (151552)
+@pytest.mark.parametrize("H,V", [(128, 256), (1152, 2048), (2304, 4096), (1152, 5120), (6144, 18944),
+                                 (640, 33152), (2048, 151552)])
 def test_fused_one_row_draft_tail_matches_split(H, V, monkeypatch):
     """One row: the fused single-kernel tail reproduces the two-launch path's
     recycled hidden, codes and scales bit for bit (the same arithmetic), and
     both paths' argmax meets the oracle (their K summation orders differ)."""
+    say(f"fused tail H={H} V={V}: {mtpd.draft_tail_plan(1, V, H)}")
     d = inputs.random_case(17 + H, 1, H, V, outliers=True)
     h, r, g, wc, ws = to_dev(d)
     fused = mtpd.draft_tail(h, r, g, d["eps"], wc, ws)
