@@ -78,9 +78,15 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
 // row_mirror (lane i takes lane 15 - i).  Each is one VALU operand modifier
 // instead of an LDS round trip, and never reads outside the row, so a row
 // that is entirely active gives the same result whatever the other rows do.
+//
+// The empty asm after each move pins it where every lane runs it: the
+// compiler otherwise may recompute a move inside a branch it makes for a
+// select, where lanes outside the branch are off and read as zero.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+    int r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
+    asm volatile("" : "+v"(r));
+    return __int_as_float(r);
 }
 
 // Maximum over each 16-lane row, in every lane of the row (exact in any
@@ -90,6 +96,21 @@ __device__ __forceinline__ float row16_max(float v) {
     v = fmaxf(v, dpp_f32<0x4E>(v));
     v = fmaxf(v, dpp_f32<0x141>(v));
     return fmaxf(v, dpp_f32<0x140>(v));
+}
+
+// u64 maximum over each 16-lane row, in every lane of the row.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t row16_max_u64(uint64_t v) {
+    v = u64_max(v, dpp_u64<0xB1>(v));
+    v = u64_max(v, dpp_u64<0x4E>(v));
+    v = u64_max(v, dpp_u64<0x141>(v));
+    return u64_max(v, dpp_u64<0x140>(v));
 }
 
 // Sum over the 64 lanes of a fully active wave with one fixed association:

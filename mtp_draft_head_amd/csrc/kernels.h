@@ -68,6 +68,15 @@ hipError_t launch_lmhead_stream(const LmheadArgs& a, int nt, int ma, int d, hipS
 // the weight-streaming kernel with a shared activation ring (lmhead_stream.hip): n_rows <= 64
 bool rows_config_compiled(int mt, int nt, int nw, int d);
 hipError_t launch_lmhead_rows(const LmheadArgs& a, int mt, int nt, int nw, int d, int cus, hipStream_t stream);
+// the same rows with K outermost and each workgroup's tmax tiles inner
+// (lmhead_stream.hip): a compiled shape for mt row tiles and V on cus CUs,
+// used when every workgroup takes at least two tiles
+struct KouterTile {
+    int nt, nw, d, tmax;
+};
+bool kouter_choose(int mt, int64_t V, int cus, KouterTile* out);
+hipError_t launch_lmhead_kouter(const LmheadArgs& a, int mt, int nt, int nw, int d, int tmax, int cus,
+                                hipStream_t stream);
 
 // multiprocessor count of the current device (cached per device)
 int device_cus();

@@ -251,6 +251,12 @@ __global__ __launch_bounds__(64 * S) void lmhead_argmax_kernel(
 }
 
 int device_cus() {
+    // "MTPD_DEVICE_CUS=n" sizes the persistent grids as if the device had n
+    // CUs (testing: several tiles per workgroup at small vocab sizes)
+    if (const char* e = getenv("MTPD_DEVICE_CUS")) {
+        const int n = atoi(e);
+        if (n > 0) return n;
+    }
     static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -407,6 +413,7 @@ bool use_stream(int64_t n_rows, int64_t V, int64_t H, int64_t a_rows, StreamTile
 
 struct RowsTile {
     int mt, nt, nw, d;
+    KouterTile ko;   // ko.tmax > 0: the K-outer kernel in that shape instead
 };
 
 // 17..64 rows, H <= stream_max_h(), 32-bit activation offsets: the streaming
@@ -434,6 +441,9 @@ bool use_rows(int64_t n_rows, int64_t V, int64_t H, int64_t a_rows, RowsTile* ou
         const RowsTile& c = cand[i];
         if (!rows_config_compiled(c.mt, c.nt, c.nw, c.d) || V % (16 * c.nt * c.nw)) continue;
         *out = c;
+        // K outermost when every workgroup takes several tiles (the activation
+        // is then copied once per workgroup, not once per tile)
+        if (!kouter_choose(c.mt, V, device_cus(), &out->ko)) out->ko = KouterTile{0, 0, 0, 0};
         return true;
     }
     return false;
@@ -467,6 +477,12 @@ void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len
     RowsTile rt;
     if (use_rows(n_rows, V, H, n_rows, &rt)) {
         const long long tiles = (long long)(V / (16 * rt.nt * rt.nw));
+        if (rt.ko.tmax > 0) {
+            const long long kt = (long long)(V / (16 * rt.ko.nt * rt.ko.nw));
+            snprintf(buf, len, "lmhead_kouter_kernel<%d,%d,%d,%d,%d> grid=%lldx%d (%lld tiles)", rt.mt, rt.ko.nt,
+                     rt.ko.nw, rt.ko.d, rt.ko.tmax, std::min<long long>(kt, device_cus()), 64 * rt.ko.nw, kt);
+            return;
+        }
         const long long grid = std::max<long long>(std::min<long long>(tiles, device_cus()), (tiles + 15) / 16);
         snprintf(buf, len, "lmhead_stream_rows_kernel<%d,%d,%d,%d> grid=%lldx%d (%lld tiles)", rt.mt, rt.nt,
                  rt.nw, rt.d, grid, 64 * rt.nw, tiles);
@@ -487,8 +503,11 @@ hipError_t launch_lmhead_argmax(const LmheadArgs& a, hipStream_t stream) {
     StreamTile st;
     if (use_stream(a.n_rows, a.V, a.H, a.a_rows, &st)) return launch_lmhead_stream(a, st.nt, st.ma, st.d, stream);
     RowsTile rt;
-    if (use_rows(a.n_rows, a.V, a.H, a.a_rows, &rt))
+    if (use_rows(a.n_rows, a.V, a.H, a.a_rows, &rt)) {
+        if (rt.ko.tmax > 0)
+            return launch_lmhead_kouter(a, rt.mt, rt.ko.nt, rt.ko.nw, rt.ko.d, rt.ko.tmax, device_cus(), stream);
         return launch_lmhead_rows(a, rt.mt, rt.nt, rt.nw, rt.d, device_cus(), stream);
+    }
     DecodeTile dt;
     if (use_decode(a.n_rows, a.V, a.H, &dt))
         return launch_lmhead_decode(a, dt.mt, dt.nt, dt.d, stream);

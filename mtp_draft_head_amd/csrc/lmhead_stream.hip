@@ -343,12 +343,15 @@ constexpr size_t rows_lds_bytes(int mt, int nt, int nw, int d) {
 // network's bit-mask mode for 4 and 8.
 template <int M>
 __device__ __forceinline__ uint32_t xor_lanes(uint32_t v) {
+    int r;
     if constexpr (M == 1)
-        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+        r = __builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
     else if constexpr (M == 2)
-        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+        r = __builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
     else
-        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (M << 10));           // and 0x1F, xor M
+        r = __builtin_amdgcn_ds_swizzle((int)v, 0x1F | (M << 10));           // and 0x1F, xor M
+    asm volatile("" : "+v"(r));   // pinned where every lane runs it (see dpp_f32)
+    return (uint32_t)r;
 }
 template <int M>
 __device__ __forceinline__ uint64_t xor_lanes_u64(uint64_t v) {
@@ -391,9 +394,7 @@ __device__ __forceinline__ void bitonic_step(uint64_t (&k0)[N], uint64_t (&k1)[N
 
 // Reverses the 16 lanes of each lane group (data-parallel row mirror).
 __device__ __forceinline__ uint64_t mirror16_u64(uint64_t v) {
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x140, 0xF, 0xF, false);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x140, 0xF, 0xF, false);
-    return ((uint64_t)hi << 32) | lo;
+    return dpp_u64<0x140>(v);
 }
 
 // Merges the descending set (n0, n1) into the descending set (r0, r1),
@@ -749,6 +750,288 @@ hipError_t launch_lmhead_rows(const LmheadArgs& a, int mt, int nt, int nw, int d
         return hipGetLastError();                                                                            \
     }
     MTPD_ROWS_CONFIGS(MTPD_X)
+#undef MTPD_X
+    return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// 17-64 rows with K outermost.  The tile-by-tile kernel above copies the
+// whole activation (64 rows x H bytes) into LDS once per 128-row weight tile,
+// a third of its copy traffic at c = 64.  Here a workgroup walks K blocks in
+// the outer loop and its TMAX tiles (b, b + G, ...) in the inner one, keeping
+// TMAX tiles' accumulators in registers, so each activation block is copied
+// once per workgroup and shared by all its tiles, and the waves meet at one
+// barrier per K block instead of one per unit.
+//
+//  - Units (block kb, tile slot i), i fastest; slots at or past the
+//    workgroup's tile count are dead (their copies repeat its last tile's
+//    block, their factor is zero), so every block walks exactly TMAX units
+//    and every register index is a compile-time constant.
+//  - Each unit's copies: the wave's NT weight tiles (2 * NT copies) and one
+//    more, either a 1 KB piece of activation block kb + 1 (the first
+//    2 * MT / NW units of the block carry its pieces) or a 4-byte placeholder,
+//    so every unit issues the same number of vector-memory operations and
+//    the waits stay compile-time counts.  Activation blocks rotate through
+//    three slots: the block in use, the next one, and the one being filled
+//    (requests run at most TMAX units ahead, so block kb + 1 is requested no
+//    earlier than block kb - 1 is in use, after the barrier that ends block
+//    kb - 2).
+//  - Promotion one unit late as in the kernel above; the keys of all tiles
+//    are formed after the stream.
+// ---------------------------------------------------------------------------
+
+template <int MT, int NT, int NW, int D, int TMAX>
+__global__ __launch_bounds__(64 * NW) void lmhead_kouter_kernel(
+    const uint8_t* __restrict__ a_codes, const float* __restrict__ a_scales,
+    const int32_t* __restrict__ row_index, int n_rows,
+    const uint8_t* __restrict__ w_codes, const float* __restrict__ w_scales, int H,
+    int total_tiles,
+    float* __restrict__ out_max, int32_t* __restrict__ out_idx, ArgmaxWs ws)
+{
+    constexpr int ROWS = MT * 16;
+    constexpr int TROWS = NW * NT * 16;      // vocab rows per tile
+    constexpr int WSLOT = NT * 2 * 64;       // uint4s per wave per unit
+    constexpr int ASLOT = MT * 2 * 64;       // uint4s per activation block
+    constexpr int DA = 3;                    // activation block slots
+    constexpr int PIECES = 2 * MT;           // 1 KB copies per activation block
+    constexpr int PW = PIECES / NW;          // pieces per wave: carried by units 0 .. PW - 1 of a block
+    static_assert(PW * NW == PIECES && PW <= TMAX, "activation pieces must split evenly over the waves");
+    static_assert(D >= 2 && D - 1 <= TMAX, "requests run at most TMAX units ahead");
+    constexpr int PER_UNIT = 2 * NT + 1;
+    static_assert((D - 2) * PER_UNIT <= 63, "vmcnt holds at most 63");
+    static_assert(TROWS <= 128 && 128 % TROWS == 0, "a tile sits inside one weight-scale block");
+    __shared__ __align__(16) uint4 wring[NW][D * WSLOT];
+    __shared__ __align__(16) uint4 aring[DA * ASLOT];
+    __shared__ __align__(16) float sw_lds[TMAX][kStreamMaxKB];
+    __shared__ unsigned int sink[NW][64];    // placeholder copies land here, never read
+    __shared__ unsigned long long red[64 * NW];
+    __shared__ int last_flag;
+    extern __shared__ __align__(16) float sa_lds[];   // [KB][ROWS], block-major
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int KB = H >> 7;
+    const int G = (int)gridDim.x;
+    const int b = (int)blockIdx.x;
+    const int ntiles = (total_tiles - b + G - 1) / G;   // 1 .. TMAX (the host sizes the grid)
+
+    uint32_t woff[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int r = 8 * q + (lane >> 3);
+            woff[nt][q] = (uint32_t)(wave * NT * 16 + nt * 16 + r) * (uint32_t)H +
+                          (uint32_t)ring_pos(r, lane & 7) * 16u;
+        }
+    // this wave's activation pieces p = wave + NW * j (rows 8p .. 8p + 7 of
+    // row tile p / 2, half p % 2), clamped to the last row
+    uint32_t aoff[PW];
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+        const int p = wave + NW * j;
+        const int r16 = 8 * (p & 1) + (lane >> 3);
+        const int m = min(8 * p + (lane >> 3), n_rows - 1);
+        aoff[j] = (uint32_t)(row_index ? row_index[m] : m) * (uint32_t)H + (uint32_t)ring_pos(r16, lane & 7) * 16u;
+    }
+    {
+        constexpr int THREADS = 64 * NW;
+        static_assert(THREADS % ROWS == 0, "each thread fills one row of the table");
+        const int row = t % ROWS;
+        const int m = min(row, n_rows - 1);
+        const uint32_t srow = (uint32_t)(row_index ? row_index[m] : m);
+        for (int kb = t / ROWS; kb < KB; kb += THREADS / ROWS) sa_lds[kb * ROWS + row] = a_scales[srow * (uint32_t)KB + kb];
+    }
+    __syncthreads();
+
+    const int fr = lane & 15, fg = lane >> 4;
+    const int fpos0 = fr * 8 + ring_pos(fr, fg);
+    const int fpos1 = fr * 8 + ring_pos(fr, fg + 4);
+    const uint32_t wring0 = lds_addr(&wring[wave][0]);
+    const uint32_t aring0 = lds_addr(aring);
+    const uint32_t sink0 = lds_addr(&sink[wave][0]);
+
+    // requests walk the units with their own counters, clamped at the last
+    // unit (units past it repeat it into slots that are never read)
+    int rkb = 0, ri = 0;
+    auto refill = [&](int slot) {
+        const int kb = rkb, i = ri;
+        const int tile = b + min(i, ntiles - 1) * G;
+        const uint8_t* wb = w_codes + (size_t)tile * TROWS * (size_t)H + (size_t)kb * kBlock;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                lds_copy16_stream(wb, woff[nt][q], wring0 + (uint32_t)(slot * WSLOT + (nt * 2 + q) * 64) * 16u);
+        if (i < PW && kb + 1 < KB) {
+            const uint32_t dst = aring0 + (uint32_t)(((kb + 1) % DA) * ASLOT + (wave + NW * i) * 64) * 16u;
+            uint32_t ao = aoff[0];
+#pragma unroll
+            for (int j = 1; j < PW; ++j) ao = i == j ? aoff[j] : ao;
+            lds_copy16(a_codes + (size_t)(kb + 1) * kBlock, ao, dst);
+        } else {
+            lds_copy4(a_scales, 0u, sink0);
+        }
+        if (kb < KB - 1 || i < TMAX - 1) {
+            if (++ri == TMAX) { ri = 0; ++rkb; }
+        }
+    };
+
+    // prologue: the tiles' weight-scale rows (lanes past KB idle), activation
+    // block 0, then units 0 .. D - 2
+    if (lane < KB) {
+        for (int i = wave; i < ntiles; i += NW)
+            lds_copy4(w_scales + (size_t)((b + i * G) * TROWS >> 7) * KB, (uint32_t)lane * 4u, lds_addr(&sw_lds[i][0]));
+    }
+#pragma unroll
+    for (int j = 0; j < PW; ++j) lds_copy16(a_codes, aoff[j], aring0 + (uint32_t)((wave + NW * j) * 64) * 16u);
+    if (lane < ROWS) red[wave * 64 + lane] = 0;
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) refill(j);
+
+    float acc[TMAX][MT][NT][4];
+#pragma unroll
+    for (int i = 0; i < TMAX; ++i)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][mt][nt][r] = 0.f;
+    v4f pp[MT][NT];
+    float4 pf[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        pf[mt] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) pp[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    // the pending unit's partials into tile slot ip's accumulators
+    auto promote = [&](int ip, int mt) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            acc[ip][mt][nt][0] = fmaf(pp[mt][nt][0], pf[mt].x, acc[ip][mt][nt][0]);
+            acc[ip][mt][nt][1] = fmaf(pp[mt][nt][1], pf[mt].y, acc[ip][mt][nt][1]);
+            acc[ip][mt][nt][2] = fmaf(pp[mt][nt][2], pf[mt].z, acc[ip][mt][nt][2]);
+            acc[ip][mt][nt][3] = fmaf(pp[mt][nt][3], pf[mt].w, acc[ip][mt][nt][3]);
+        }
+    };
+
+    int cslot = 0;
+    v8i af[MT];       // the block's activation fragments, read at its first unit
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i) {
+            wait_vm((D - 2) * PER_UNIT);   // this wave's copies of this unit (and all older ones)
+            if (i == 0) {                  // everyone's copies of activation block kb; all past block kb - 1
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+            }
+            refill(cslot == 0 ? D - 1 : cslot - 1);
+            if (i == 0) {
+                const uint4* ta = &aring[(kb % DA) * ASLOT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) af[mt] = make_frag(ta[mt * 128 + fpos0], ta[mt * 128 + fpos1]);
+            }
+            const float sw = i < ntiles ? sw_lds[i][kb] : 0.f;
+            const uint4* tw = &wring[wave][cslot * WSLOT];
+            v8i bf[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) bf[nt] = make_frag(tw[nt * 128 + fpos0], tw[nt * 128 + fpos1]);
+            const int ip = i == 0 ? TMAX - 1 : i - 1;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const float4 sa4 = *reinterpret_cast<const float4*>(&sa_lds[kb * ROWS + mt * 16 + 4 * fg]);
+                v4f p[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) p[nt] = mfma_e4m3(af[mt], bf[nt]);
+                promote(ip, mt);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) pp[mt][nt] = p[nt];
+                pf[mt] = make_float4(sa4.x * sw, sa4.y * sw, sa4.z * sw, sa4.w * sw);
+            }
+            cslot = cslot + 1 == D ? 0 : cslot + 1;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) promote(TMAX - 1, mt);
+    MTPD_WAIT_VM(0);   // the clamped tail requests, before LDS is reused
+
+    // per-row best over this wave's columns of every live tile: per lane
+    // over the tiles first, then one 16-lane maximum per row
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            uint64_t best = 0;
+#pragma unroll
+            for (int i = 0; i < TMAX; ++i) {
+                const uint32_t n0 = (uint32_t)((b + i * G) * TROWS + wave * NT * 16 + (lane & 15));
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const uint64_t k = argmax_key(acc[i][mt][nt][r], n0 + (uint32_t)(nt * 16));
+                    best = i < ntiles ? u64_max(best, k) : best;
+                }
+            }
+            best = row16_max_u64(best);
+            if ((lane & 15) == 0) red[wave * 64 + mt * 16 + 4 * (lane >> 4) + r] = best;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    __syncthreads();
+    if (wave == 0) {
+        uint64_t old = 0;
+        if (lane < ROWS && lane < n_rows) {
+            uint64_t k = red[lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) k = u64_max(k, red[w * 64 + lane]);
+            old = merge_key(ws, n_rows, b, lane, k);
+        }
+        const unsigned int dep = __builtin_amdgcn_ballot_w64(never_nonzero(old) != 0) != 0 ? 1u : 0u;
+        if (lane == 0) last_flag = arrive(ws, b, G, dep) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    finalize_argmax<64 * NW>(ws, n_rows, out_max, out_idx, red);
+}
+
+#define MTPD_KOUTER_CONFIGS(X) X(4, 1, 8, 4, 4)
+
+bool kouter_choose(int mt, int64_t V, int cus, KouterTile* out) {
+    const char* e = getenv("MTPD_LMHEAD_KOUTER");   // "0": never; "nt,nw,d,tmax": that shape only (testing)
+    KouterTile want{0, 0, 0, 0};
+    if (e && strcmp(e, "0") == 0) return false;
+    if (e) sscanf(e, "%d,%d,%d,%d", &want.nt, &want.nw, &want.d, &want.tmax);
+#define MTPD_X(a, b2, c2, e2, f)                                                                              \
+    if (mt == a && V % (16 * b2 * c2) == 0 && (want.nt == 0 || (want.nt == b2 && want.nw == c2 &&            \
+                                                                  want.d == e2 && want.tmax == f))) {        \
+        const int64_t tiles = V / (16 * b2 * c2), g = std::min<int64_t>(tiles, cus);                         \
+        if (tiles >= 2 * g - 1 && (tiles + g - 1) / g == f) {                                                 \
+            *out = KouterTile{b2, c2, e2, f};                                                                 \
+            return true;                                                                                      \
+        }                                                                                                     \
+    }
+    MTPD_KOUTER_CONFIGS(MTPD_X)
+#undef MTPD_X
+    return false;
+}
+
+hipError_t launch_lmhead_kouter(const LmheadArgs& a, int mt, int nt, int nw, int d, int tmax, int cus,
+                                hipStream_t stream) {
+    const int64_t tiles = a.V / (16 * nt * nw);
+    if (tiles < 1 || tiles > 0x7FFFFFFF || a.H > kStreamMaxH || a.n_rows > 16 * mt) return hipErrorInvalidValue;
+    const int64_t grid = std::min<int64_t>(tiles, cus);
+    if ((tiles + grid - 1) / grid > tmax) return hipErrorInvalidValue;   // at most tmax tiles per workgroup
+    const size_t lds = (size_t)(16 * mt) * (size_t)(a.H / kBlock) * sizeof(float);
+#define MTPD_X(p, q, r, u, v)                                                                                \
+    if (mt == p && nt == q && nw == r && d == u && tmax == v) {                                              \
+        hipLaunchKernelGGL((lmhead_kouter_kernel<p, q, r, u, v>), dim3((unsigned)grid), dim3(64 * r), lds,   \
+                           stream, a.a_codes, a.a_scales, a.row_index, (int)a.n_rows, a.w_codes, a.w_scales, \
+                           (int)a.H, (int)tiles, a.out_max, a.out_idx, argmax_ws(a.workspace, a.n_rows));   \
+        return hipGetLastError();                                                                            \
+    }
+    MTPD_KOUTER_CONFIGS(MTPD_X)
 #undef MTPD_X
     return hipErrorInvalidValue;
 }

@@ -237,6 +237,41 @@ def test_stream_rows_kernel_shapes(M, shape, monkeypatch):
     assert torch.equal(i0, i1)
 
 
+# (M, H, V, CUs): the persistent grid sized for `cus` CUs gives every
+# workgroup 4 tiles (4096 / 128 on 8, 3584 / 128 on 7) or 3 to 4 (on 9, so
+# some workgroups run dead tile slots); ragged K (H = 2176) and M
+@pytest.mark.parametrize("M,H,V,cus", [(64, 1024, 4096, 8), (33, 2176, 4096, 8), (48, 640, 3584, 7),
+                                       (64, 1152, 4096, 9)])
+def test_kouter_kernel_shapes(M, H, V, cus, monkeypatch):
+    """33..64 rows with K outermost (each workgroup's tiles share one copy of
+    every activation block): meets the oracle and picks the decode kernel's
+    indices."""
+    d = inputs.random_case(31 + M + cus, M, H, V, outliers=True)
+    h, r, g, wc, ws = to_dev(d)
+    monkeypatch.setenv("MTPD_LMHEAD_KERNEL", "decode")
+    _, codes, scales, m0, i0 = mtpd.draft_tail(h, r, g, d["eps"], wc, ws)
+    monkeypatch.delenv("MTPD_LMHEAD_KERNEL")
+    monkeypatch.setenv("MTPD_DEVICE_CUS", str(cus))
+    plan = mtpd.lmhead_plan(M, V, H)
+    say(f"  plan: {plan}")
+    assert plan.startswith("lmhead_kouter_kernel")
+    m1, i1 = mtpd.fp8_lmhead_argmax(codes, scales, wc, ws)
+    torch.cuda.synchronize()
+    check_lmhead(codes, scales, d, m1, i1)
+    assert torch.equal(i0, i1)
+
+
+def test_kouter_kernel_full_width():
+    """64 rows, H = 6144, V = 131072 on the device's own CU count (1024
+    tiles: four per workgroup on 256 CUs), sampled rows against the oracle."""
+    M, H, V = 64, 6144, 131072
+    d = inputs.random_case(77, M, H, V, outliers=True)
+    h, r, g, wc, ws = to_dev(d)
+    say(f"  plan: {mtpd.lmhead_plan(M, V, H)}")
+    _, codes, scales, m, i = mtpd.draft_tail(h, r, g, d["eps"], wc, ws)
+    check_lmhead(codes, scales, d, m, i, rows=np.array([0, 17, 40, 63]))
+
+
 def test_stream_rows_kernel_vocab_shard_shape(workloads):
     """64 rows on one GPU's 18944-row vocab shard (the decode c=64 weight's
     first 148 blocks): every row against the oracle."""
