@@ -776,8 +776,9 @@ hipError_t launch_lmhead_rows(const LmheadArgs& a, int mt, int nt, int nw, int d
 //    (requests run at most TMAX units ahead, so block kb + 1 is requested no
 //    earlier than block kb - 1 is in use, after the barrier that ends block
 //    kb - 2).
-//  - Promotion one unit late as in the kernel above; the keys of all tiles
-//    are formed after the stream.
+//  - Each unit's partials are promoted at once; the keys of all tiles are
+//    formed after the stream, per lane over the tiles first and then one
+//    16-lane maximum per row.
 // ---------------------------------------------------------------------------
 
 template <int MT, int NT, int NW, int D, int TMAX>
@@ -901,13 +902,9 @@ __global__ __launch_bounds__(64 * NW) void lmhead_kouter_kernel(
                 for (int r = 0; r < 4; ++r) acc[i][mt][nt][r] = 0.f;
     v4f pp[MT][NT];
     float4 pf[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        pf[mt] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) pp[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
-    // the pending unit's partials into tile slot ip's accumulators
+    // a unit's partials into tile slot ip's accumulators (at once: carrying
+    // them to the next unit, as the kernel above does, costs registers this
+    // kernel does not have)
     auto promote = [&](int ip, int mt) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -939,24 +936,18 @@ __global__ __launch_bounds__(64 * NW) void lmhead_kouter_kernel(
             v8i bf[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) bf[nt] = make_frag(tw[nt * 128 + fpos0], tw[nt * 128 + fpos1]);
-            const int ip = i == 0 ? TMAX - 1 : i - 1;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const float4 sa4 = *reinterpret_cast<const float4*>(&sa_lds[kb * ROWS + mt * 16 + 4 * fg]);
-                v4f p[NT];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) p[nt] = mfma_e4m3(af[mt], bf[nt]);
-                promote(ip, mt);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) pp[mt][nt] = p[nt];
+                for (int nt = 0; nt < NT; ++nt) pp[mt][nt] = mfma_e4m3(af[mt], bf[nt]);
                 pf[mt] = make_float4(sa4.x * sw, sa4.y * sw, sa4.z * sw, sa4.w * sw);
+                promote(i, mt);
             }
             cslot = cslot + 1 == D ? 0 : cslot + 1;
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) promote(TMAX - 1, mt);
     MTPD_WAIT_VM(0);   // the clamped tail requests, before LDS is reused
 
     // per-row best over this wave's columns of every live tile: per lane
@@ -996,7 +987,7 @@ __global__ __launch_bounds__(64 * NW) void lmhead_kouter_kernel(
     finalize_argmax<64 * NW>(ws, n_rows, out_max, out_idx, red);
 }
 
-#define MTPD_KOUTER_CONFIGS(X) X(4, 1, 8, 4, 4)
+#define MTPD_KOUTER_CONFIGS(X) X(4, 1, 8, 4, 4) X(4, 2, 4, 5, 5)
 
 bool kouter_choose(int mt, int64_t V, int cus, KouterTile* out) {
     const char* e = getenv("MTPD_LMHEAD_KOUTER");   // "0": never; "nt,nw,d,tmax": that shape only (testing)

@@ -238,10 +238,11 @@ def test_stream_rows_kernel_shapes(M, shape, monkeypatch):
 
 
 # (M, H, V, CUs): the persistent grid sized for `cus` CUs gives every
-# workgroup 4 tiles (4096 / 128 on 8, 3584 / 128 on 7) or 3 to 4 (on 9, so
-# some workgroups run dead tile slots); ragged K (H = 2176) and M
+# workgroup 4 tiles (4096 / 128 on 8, 3584 / 128 on 7), 3 to 4 (on 9, so
+# some workgroups run dead tile slots), 5 (5120 on 8) or 4 to 5 (4608 on 8);
+# ragged K (H = 2176) and M
 @pytest.mark.parametrize("M,H,V,cus", [(64, 1024, 4096, 8), (33, 2176, 4096, 8), (48, 640, 3584, 7),
-                                       (64, 1152, 4096, 9)])
+                                       (64, 1152, 4096, 9), (64, 1024, 5120, 8), (40, 2176, 4608, 8)])
 def test_kouter_kernel_shapes(M, H, V, cus, monkeypatch):
     """33..64 rows with K outermost (each workgroup's tiles share one copy of
     every activation block): meets the oracle and picks the decode kernel's
