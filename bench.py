@@ -63,6 +63,7 @@ CSRC = "mtp_draft_head_amd/csrc/"
 KERNEL_SOURCE = {"lmhead_gemm_kernel": "lmhead_gemm.hip", "lmhead_decode_kernel": "lmhead_decode.hip",
                  "lmhead_argmax_kernel": "lmhead_argmax.hip", "lmhead_stream_kernel": "lmhead_stream.hip",
                  "lmhead_stream_rows_kernel": "lmhead_stream.hip", "draft_tail1_kernel": "lmhead_stream.hip",
+                 "lmhead_kouter_kernel": "lmhead_stream.hip",
                  "allreduce_norm_quant_kernel": "norm_quant.hip", "norm_quant_kernel": "norm_quant.hip",
                  "argmax_combine_kernel": "argmax_combine.hip"}
 SHARED_HEADERS = ["lmhead_common.h", "device_common.h", "kernels.h"]
