@@ -190,8 +190,7 @@ __global__ __launch_bounds__(256) void lmhead_decode_kernel(
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
                 best = u64_max(best, argmax_key(acc[mt][nt][i], (uint32_t)(n0 + nt * 16 + (lane & 15))));
-#pragma unroll
-            for (int off = 8; off > 0; off >>= 1) best = u64_max(best, shfl_xor_u64(best, off));
+            best = row16_max_u64(best);
             if ((lane & 15) == 0) red[wave * ROWS + mt * 16 + 4 * (lane >> 4) + i] = best;
         }
     }

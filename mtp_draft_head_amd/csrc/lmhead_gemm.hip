@@ -256,8 +256,7 @@ __global__ __launch_bounds__(512) void lmhead_gemm_kernel(
             for (int nt = 0; nt < 4; ++nt)
                 best = u64_max(best, argmax_key(acc[mt][nt][i],
                                                 (uint32_t)(n0 + wn * 64 + nt * 16 + (lane & 15))));
-#pragma unroll
-            for (int off = 8; off > 0; off >>= 1) best = u64_max(best, shfl_xor_u64(best, off));
+            best = row16_max_u64(best);
             if ((lane & 15) == 0) red[wn * kBM + wm * 128 + mt * 16 + 4 * (lane >> 4) + i] = best;
         }
     }

@@ -280,8 +280,7 @@ __global__ __launch_bounds__(64) void lmhead_stream_kernel(
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             best = u64_max(best, argmax_key(acc[nt][i], (uint32_t)(n0 + nt * 16 + (lane & 15))));
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) best = u64_max(best, shfl_xor_u64(best, off));
+        best = row16_max_u64(best);
         if ((lane & 15) == 0) red[4 * (lane >> 4) + i] = best;
     }
     __syncthreads();
@@ -646,8 +645,7 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_rows_kernel(
                     best = u64_max(best, argmax_key(acc[mt][nt][r], (uint32_t)(n0 + nt * 16 + (lane & 15))));
                     acc[mt][nt][r] = 0.f;
                 }
-#pragma unroll
-                for (int off = 8; off > 0; off >>= 1) best = u64_max(best, shfl_xor_u64(best, off));
+                best = row16_max_u64(best);
                 if ((lane & 15) == 0) {
                     unsigned long long* slot = &red[wave * 64 + mt * 16 + 4 * (lane >> 4) + r];
                     *slot = u64_max(*slot, best);
@@ -1425,8 +1423,7 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
         if (t < KB) scales[t] = sa_lds[t];
     }
     if (wave == 0) {
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) best = u64_max(best, shfl_xor_u64(best, off));
+        best = row16_max_u64(best);
         uint64_t old = 0;
         if (lane == 0) old = merge_key(ws, 1, b, 0, best);
         const unsigned int dep = __builtin_amdgcn_ballot_w64(never_nonzero(old) != 0) != 0 ? 1u : 0u;
