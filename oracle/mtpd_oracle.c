@@ -29,9 +29,10 @@
  *     Equal maxima resolve to the lowest index.
  *
  * Arithmetic is fp64 throughout, except where the result is defined as an
- * fp32 value (the scales, the quantization quotient that the 8-bit code is
- * decided on, the logit the argmax is decided on).  Those decisions are
- * taken in fp32, the precision the GPU takes them in.
+ * fp32 value: the block scales (an fp32 dequant multiplier) and the logit
+ * the argmax is decided on (logits are fp32 and never materialized, so the
+ * draft token is the first index of the largest fp32 logit).  The 8-bit
+ * code is the E4M3 rounding of the fp64 quotient y / scale, rounded once.
  *
  * Parity pins for every function here live in tests/ (codecs against the
  * library casts of torch, RMSNorm closed forms, quantization invariants,
@@ -178,7 +179,8 @@ void ora_bf16_encode_array(const double *x, int64_t n, uint16_t *out)
  * Quantize one row y[0..H) (H a multiple of 128):
  *   amax  = max |y_j| over the block
  *   scale = RN_f32(amax / 448), the dequant multiplier (y ~ dec(code) * scale)
- *   code  = E4M3(RN_f32(y_j / scale)), saturating, ties to even
+ *   code  = E4M3(y_j / scale), the fp64 quotient rounded once to the
+ *           nearest E4M3FN value, ties to even, saturating at +-448
  * A block whose scale is zero (amax zero, or so small the quotient underflows
  * fp32) gets scale 0 and all-zero codes.
  */
@@ -197,8 +199,7 @@ static void ora_block_quant_row(const double *y, int64_t H, uint8_t *codes, floa
             if (scale == 0.0f) {
                 codes[j] = 0x00;
             } else {
-                float quotient = (float)(y[j] / (double)scale);
-                codes[j] = ora_e4m3_encode((double)quotient);
+                codes[j] = ora_e4m3_encode(y[j] / (double)scale);
             }
         }
     }

@@ -139,13 +139,13 @@ def _quant_invariants(y, codes, scales):
     # scale is RN_f32(amax / 448)
     assert np.array_equal(scales, (amax / 448.0).astype(np.float32))
     nz = scales > 0
-    # (i) reconstruction error: at most half the e4m3 spacing at y/scale, times scale,
-    # plus the fp32 rounding of the quotient the code is decided on
+    # (i) reconstruction error: at most half the e4m3 spacing at y/scale, times
+    # scale (the code is y/scale rounded once; the 1e-12 covers the fp64 quotient)
     q = np.where(nz[:, :, None], yb / np.where(nz, s64, 1.0)[:, :, None], 0.0)
     aq = np.abs(q)
     e = np.floor(np.log2(np.maximum(aq, 2.0 ** -6)))
     spacing = np.ldexp(1.0, (e - 3).astype(int))
-    bound = (spacing / 2 + aq * 2.0 ** -23) * s64[:, :, None]
+    bound = spacing / 2 * s64[:, :, None]
     err = np.abs(dq.reshape(M, KB, 128) - yb)
     assert np.all(err[nz] <= bound[nz] * (1 + 1e-12))
     # (ii) each nonzero block holds a code of magnitude 448
@@ -168,6 +168,32 @@ def test_block_quant_invariants_and_idempotence():
     c2, s2 = oracle.block_quant(dequant_f64(codes, scales))
     assert np.array_equal(s2, scales)
     assert np.array_equal(c2, codes)
+
+
+def test_code_is_the_quotient_rounded_once():
+    """The code is E4M3(y / scale) with the fp64 quotient rounded once.  Next to
+    an E4M3 midpoint, a quotient first rounded to fp32 lands on the midpoint
+    and then goes to the even neighbour; rounding once must not.  In [4, 8)
+    the E4M3 spacing is 0.5: 4.75 lies between 4.5 (0x49, odd mantissa) and
+    5.0 (0x4A), 4.25 between 4.0 (0x48) and 4.5.  2^-30 is below half an fp32
+    ulp at 4 (2^-21), so RN_f32 of each quotient below is the midpoint itself."""
+    d = 2.0 ** -30
+    for k in (1.0, 3.0, 0.0625):                  # scales 1, 3, 1/16: quotients stay exact in fp64
+        y = np.zeros((1, 128))
+        y[0, 0] = 448.0 * k                       # amax: scale = RN_f32(448k/448) = k
+        y[0, 1] = (4.75 - d) * k                  # just below the odd/even midpoint: down to 4.5
+        y[0, 2] = (4.25 + d) * k                  # just above the even/odd midpoint: up to 4.5
+        y[0, 3] = -(4.75 - d) * k
+        y[0, 4] = 4.75 * k                        # exactly on the midpoint: ties to even, 5.0
+        y[0, 5] = 4.25 * k                        # exactly on the midpoint: ties to even, 4.0
+        y[0, 6] = (2.0 ** -9 * 1.5 - 2.0 ** -40) * k   # just below a subnormal midpoint: 1 * 2^-9
+        y[0, 7] = (2.0 ** -9 * 2.5 + 2.0 ** -40) * k   # just above one: 3 * 2^-9
+        codes, scales = oracle.block_quant(y)
+        assert scales[0, 0] == np.float32(k)
+        assert codes[0, :8].tolist() == [0x7E, 0x49, 0x49, 0xC9, 0x4A, 0x48, 0x01, 0x03], (k, codes[0, :8])
+        # the fp32 quotient would have decided otherwise on the first two
+        q32 = (y[0, 1:3] / k).astype(np.float32)
+        assert q32.tolist() == [4.75, 4.25]
 
 
 def test_idempotence_fails_if_dequant_is_rounded_to_bf16():
