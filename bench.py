@@ -3,8 +3,14 @@
 
 A step is one mtpd_draft_tail call (residual add + RMSNorm + packed FP8,
 then the block-scaled FP8 LM head with the fused argmax) over one batch of
-synthetic input already resident in HBM.  Default workload: decode c=1 on one
-GPU's TP8 vocab shard (M=1, H=6144, V=18944).
+synthetic input already resident in HBM.  Default workload: the largest
+single-GPU configuration, the compute-bound stress case (M=8192, H=6144,
+V=151552), whose roofline is the FP8 MFMA peak.  The two decode
+configurations that share its weight (c=64 on the full vocab, M=64; c=1 on
+one GPU's TP8 vocab shard, M=1, V=18944) are timed in the same run and
+reported as extra keys against the HBM peak ("companions").  Measured
+achievable peaks (a streaming read of HBM and a loop of the same FP8 MFMA)
+are reported beside the published ones ("measured_peaks").
 
 Timing: W eager warmup steps, then K steps captured in one HIP graph and
 replayed once, bracketed by device synchronizations and HIP events on the
@@ -60,7 +66,8 @@ CACHE_DEFEAT_BYTES = 768 << 20  # rotate weight copies past the 256 MB Infinity 
 CSRC = "mtp_draft_head_amd/csrc/"
 # the source a kernel is defined in; a traffic summary stays valid while that
 # file and the shared headers are unchanged
-KERNEL_SOURCE = {"lmhead_gemm_kernel": "lmhead_gemm.hip", "lmhead_decode_kernel": "lmhead_decode.hip",
+KERNEL_SOURCE = {"lmhead_gemm_kernel": "lmhead_gemm.hip", "lmhead_gemm2_kernel": "lmhead_gemm.hip",
+                 "lmhead_decode_kernel": "lmhead_decode.hip",
                  "lmhead_argmax_kernel": "lmhead_argmax.hip", "lmhead_stream_kernel": "lmhead_stream.hip",
                  "lmhead_stream_rows_kernel": "lmhead_stream.hip", "draft_tail1_kernel": "lmhead_stream.hip",
                  "lmhead_kouter_kernel": "lmhead_stream.hip",
@@ -234,8 +241,9 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, copy_mib: int, 
 def cpu_baseline(d, seconds: float, variant: str = "tail", parts=None):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     the variant's full tail (norm + pack + LM head + argmax, with the partial
-    sum or the shard combine where the variant has one) for n rows drawn
-    cyclically from the workload's rows, n sized to take about `seconds`."""
+    sum or the shard combine where the variant has one) for n rows, n sized
+    to take about `seconds`: a seeded draw of n distinct rows when n is below
+    the workload's row count, else its rows taken cyclically."""
     import numpy as np
 
     import oracle
@@ -243,8 +251,13 @@ def cpu_baseline(d, seconds: float, variant: str = "tail", parts=None):
     w = d["workload"]
     H, V = w.H, w.V
 
+    def pick(n):
+        if n < w.M:
+            return np.sort(np.random.default_rng(1234).choice(w.M, size=n, replace=False))
+        return np.arange(n) % w.M
+
     def run(n):
-        rows = np.arange(n) % w.M
+        rows = pick(n)
         t0 = time.perf_counter()
         if variant == "allreduce_tail":
             nq = oracle.allreduce_norm_quant(parts[:, rows], d["residual"][rows], d["norm_weight"], d["eps"])
@@ -265,16 +278,69 @@ def cpu_baseline(d, seconds: float, variant: str = "tail", parts=None):
             "topk": f"norm + pack + LM head + top-{TOPK_K}", "vocab_shards": f"full tail with {N_SHARDS} vocab shards combined",
             "allreduce_tail": f"full tail with the {N_PARTIALS}-partial sum"}[variant]
     return {"value": n / t, "unit": "rows/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{n} rows of {w.name} (M={w.M} H={H} V={V}, rows taken cyclically), {what} "
+            "sample": f"{n} rows of {w.name} (M={w.M} H={H} V={V}, "
+                      f"{'a seeded draw of distinct rows' if n < w.M else 'rows taken cyclically'}), {what} "
                       f"incl. the whole {V}-row LM head per row, fp64, {t:.1f} s"}
+
+
+def measure_peaks(dev, log_fn):
+    """Achievable peaks measured on this GPU by libmtpd_peaks: a streaming
+    read of a 4 GiB buffer (non-temporal 16-byte loads, 4096 workgroups) and
+    a register-only loop of the 16x16x128 E4M3 MFMA (1024 workgroups of 4
+    waves, 8 independent accumulations each); best of 5 launches each."""
+    import ctypes
+
+    import torch
+
+    from mtp_draft_head_amd import build as lib_build
+
+    path = lib_build.peaks_library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built")
+    L = ctypes.CDLL(path)
+    L.mtpd_peak_read.restype = ctypes.c_int
+    L.mtpd_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.mtpd_peak_mfma.restype = ctypes.c_int
+    L.mtpd_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream(dev)
+    nbytes, grid = 4 << 30, 4096
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+    mgrid, iters = 1024, 2048
+    mout = torch.empty(mgrid * 256, dtype=torch.float32, device=dev)
+
+    def best(fn, n=5):
+        times = []
+        for _ in range(n + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if fn() != 0:
+                raise RuntimeError("peak probe launch failed")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        return min(times[1:])
+
+    log_fn("[bench] measuring achievable peaks (HBM streaming read, FP8 MFMA loop)")
+    t_read = best(lambda: L.mtpd_peak_read(buf.data_ptr(), nbytes, grid, sink.data_ptr(), stream.cuda_stream))
+    t_mfma = best(lambda: L.mtpd_peak_mfma(iters, mgrid, mout.data_ptr(), stream.cuda_stream))
+    flops = mgrid * 4 * iters * 8 * 65536.0
+    del buf, sink, mout
+    return {"hbm_read_GBps": round(nbytes / t_read / 1e9, 1),
+            "fp8_mfma_TFLOPs": round(flops / t_mfma / 1e12, 1),
+            "how": "streaming read of 4 GiB (4096 workgroups, nt 16-byte loads); register-only loop of "
+                   "v_mfma_f32_16x16x128_f8f6f4 (1024 workgroups x 4 waves x 8 accumulations); best of 5"}
 
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_c1_tp8_shard")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="compute_stress")
+    ap.add_argument("--no-companions", action="store_true",
+                    help="skip timing the decode configurations that share the workload's weight")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured achievable peaks")
     ap.add_argument("--variant", default="tail", choices=["tail", "vocab_shards", "allreduce_tail", "chain", "topk"])
     ap.add_argument("--topk", type=int, default=8, help="k of the topk variant (1..32)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -327,7 +393,7 @@ def main() -> int:
            torch.empty((M,), dtype=torch.float32, device=dev),
            torch.empty((M,), dtype=torch.int32, device=dev))
     lm_out = (torch.empty((M,), dtype=torch.float32, device=dev), torch.empty((M,), dtype=torch.int32, device=dev))
-    wsp = mtpd.Workspace(dev)
+    wsp = mtpd.Workspace(dev, any_stream=True)   # eager warmup and graph capture share it, in order
     wsp.get(M)
     K, W = args.steps, args.warmup
     extra = {}
@@ -348,7 +414,7 @@ def main() -> int:
     elif variant == "topk":
         tk_out = (torch.empty((M, TOPK_K), dtype=torch.float32, device=dev),
                   torch.empty((M, TOPK_K), dtype=torch.int32, device=dev))
-        tk_ws = mtpd.Workspace(dev)
+        tk_ws = mtpd.Workspace(dev, any_stream=True)
         tk_ws.get_bytes(mtpd.topk_workspace_bytes(M, V, TOPK_K))
 
         def step(i):
@@ -510,6 +576,66 @@ def main() -> int:
         lm_us = None
     lm_alg = lmhead_bytes(M, H, V)
 
+    # the decode configurations that share this workload's weight, timed the
+    # same way (a graph of K steps, weight copies rotated past the cache)
+    companions = {}
+    if variant == "tail" and not args.no_companions:
+        for cname in ("decode_c64_full", "decode_c1_tp8_shard"):
+            cw = inputs.get(cname)
+            if cname == w.name or cw.H != H or cw.v_full != w.v_full or cw.V > V:
+                continue
+            cd = inputs.make(cname)
+            assert np.array_equal(cd["w_codes"][:256], d["w_codes"][:256])   # the same weight family
+            Mc, Vc = cw.M, cw.V
+            ch = torch.from_numpy(cd["hidden"].view(np.int16)).to(dev).view(torch.bfloat16)
+            cr = torch.from_numpy(cd["residual"].view(np.int16)).to(dev).view(torch.bfloat16)
+            cg = torch.from_numpy(cd["norm_weight"]).to(dev)
+            nc = max(1, math.ceil(CACHE_DEFEAT_BYTES / (Vc * H)))
+            cwc = [wc0[:Vc]] + [wc0[:Vc].clone() for _ in range(nc - 1)]
+            cws = [ws0[:Vc // 128]] + [ws0[:Vc // 128].clone() for _ in range(nc - 1)]
+            cout = (torch.empty((Mc, H), dtype=torch.bfloat16, device=dev),
+                    torch.empty((Mc, H), dtype=torch.uint8, device=dev),
+                    torch.empty((Mc, H // 128), dtype=torch.float32, device=dev),
+                    torch.empty((Mc,), dtype=torch.float32, device=dev),
+                    torch.empty((Mc,), dtype=torch.int32, device=dev))
+            clm = (torch.empty((Mc,), dtype=torch.float32, device=dev),
+                   torch.empty((Mc,), dtype=torch.int32, device=dev))
+
+            def cstep(i, ch=ch, cr=cr, cg=cg, cwc=cwc, cws=cws, cout=cout, nc=nc, eps=cd["eps"]):
+                mtpd.draft_tail(ch, cr, cg, eps, cwc[i % nc], cws[i % nc], workspace=wsp, out=cout)
+
+            def cker(i, cwc=cwc, cws=cws, cout=cout, clm=clm, nc=nc):
+                mtpd.fp8_lmhead_argmax(cout[1], cout[2], cwc[i % nc], cws[i % nc], workspace=wsp, out=clm)
+
+            log(f"[bench] companion {cname}: M={Mc} V={Vc}, {nc} weight copies; timing {K} steps")
+            for i in range(W):
+                cstep(i)
+            ms_cs, gc1 = timed_graph(cstep)
+            cref = cout[4].clone()
+            cstep(0)
+            torch.cuda.synchronize()
+            assert torch.equal(cref, cout[4]), "companion graph replay and eager call disagree"
+            ms_ck, gc2 = timed_graph(cker)
+            del gc1, gc2
+            ckname, ckind, calg, ckplan, _ = roofline_kernel("tail", Mc, H, Vc)
+            ck_us = ms_cs * 1e3 if ckind == "tail" else ms_ck * 1e3
+            cgbps = calg / (ck_us * 1e-6) / 1e9
+            lm_alg_c = lmhead_bytes(Mc, H, Vc)
+            companions[cname] = {
+                "M": Mc, "H": H, "V": Vc, "weight_copies_rotated": nc,
+                "ms_per_step": round(ms_cs, 5), "rows_per_s": round(Mc / (ms_cs * 1e-3), 1),
+                "draft_tail_plan": mtpd.draft_tail_plan(Mc, Vc, H),
+                "roofline": {"bound": "hbm", "achieved": round(cgbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": round(cgbps / HBM_PEAK_GBPS, 4),
+                             "traffic": traffic_from_profile(ckname, cname, "tail"),
+                             "kernel": ckplan, "avg_launch_us": round(ck_us, 3),
+                             "algorithmic_bytes_per_launch": calg},
+                "lmhead": {"kernel": mtpd.lmhead_plan(Mc, Vc, H), "us": round(ms_ck * 1e3, 3),
+                           "hbm_frac": round(lm_alg_c / (ms_ck * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+            }
+            del cwc, cws, cout
+    peaks = None if args.no_peaks else measure_peaks(dev, log)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle (~{args.cpu_seconds:.0f} s)")
@@ -545,6 +671,14 @@ def main() -> int:
                          "hbm_frac": round(lm_alg / (lm_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                          "fp8_frac": round(flops / (lm_us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4)}
     rec.update(extra)
+    if peaks is not None:
+        roof["frac_of_measured"] = round(roof["achieved"] / (peaks["fp8_mfma_TFLOPs"] if roof["unit"] == "TFLOP/s"
+                                                             else peaks["hbm_read_GBps"]), 4)
+        for c in companions.values():
+            c["roofline"]["frac_of_measured"] = round(c["roofline"]["achieved"] / peaks["hbm_read_GBps"], 4)
+        rec["measured_peaks"] = peaks
+    if companions:
+        rec["companions"] = companions
     rec.update({"eager_ms_per_step": round(eager_ms, 5), "roofline": roof, "cpu_baseline": cpu})
     print(json.dumps(rec), flush=True)
     return 0

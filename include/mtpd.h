@@ -134,8 +134,15 @@ mtpd_status mtpd_fp8_lmhead_argmax(const mtpd_qact *act, const int32_t *row_inde
 /*
  * The whole draft tail for M rows: mtpd_norm_quant followed by
  * mtpd_fp8_lmhead_argmax on every row of the packed activation it produced
- * (row_index NULL).  Same arguments, layouts, workspace contract and
- * results as the two calls in sequence; w->H must equal H.
+ * (row_index NULL).  This is the producer/consumer pair of
+ * "[Quant][MTP] Reuse packed FP8 logits inputs", Purpose (the MTP layer
+ * returns the packed activation and the bf16 hidden; the shared LM head
+ * consumes the packed activation as it is) closed by the local greedy
+ * argmax of "[Spec Decode][Perf] Fuse the MTP trailing all-reduce;
+ * local-argmax draft tokens", Summary.  Same arguments, layouts, workspace
+ * contract and results as the two calls in sequence; w->H must equal H.
+ * One row with H <= 6144 runs as a single fused launch whose recycled
+ * hidden, codes and scales are bit-identical to the two-launch path.
  */
 mtpd_status mtpd_draft_tail(const uint16_t *hidden, const uint16_t *residual,
                             const float *norm_weight, float eps, int64_t M, int64_t H,
@@ -230,7 +237,10 @@ size_t mtpd_workspace_bytes(int64_t n_rows);
 const char *mtpd_status_name(mtpd_status s);
 
 /* Detail of the first failure on the calling thread since the last
- * mtpd_clear_error (empty string if none).  The pointer stays valid until
+ * mtpd_clear_error (empty string if none).  The first failure is kept, not
+ * the latest, so the root cause survives the errors it provokes (the
+ * practice "feat(glm52): add checkpoint-native MTP speculative decoding",
+ * Description, follows for its own failures).  The pointer stays valid until
  * the next mtpd_clear_error on this thread. */
 const char *mtpd_last_error(void);
 void mtpd_clear_error(void);
@@ -246,6 +256,32 @@ const char *mtpd_lmhead_plan(int64_t n_rows, int64_t V, int64_t H);
  * "norm_quant_kernel<3> grid=64x256 + lmhead_stream_rows_kernel<4,2,4,3>
  * grid=1184x256"; same string rules as mtpd_lmhead_plan. */
 const char *mtpd_draft_tail_plan(int64_t M, int64_t V, int64_t H);
+
+/*
+ * Launch-plan override, for tuning sweeps and tests only: pins the kernel
+ * (or launch shape) the dispatcher picks, so that every compiled shape can be
+ * checked against the same results.  Results stay within the documented
+ * tolerances under any setting; only the speed and the fp32 summation order
+ * change.  Process-wide, read by the host-side dispatch of every later call:
+ * set it only while no call of this library is being made on any thread.
+ *
+ *   key               value
+ *   "lmhead_kernel"   "generic" (the generic tiled kernel only) or "decode"
+ *                     (no weight-streaming kernels), NULL for automatic
+ *   "lmhead_tile"     "nt,s,d"       generic kernel shape
+ *   "lmhead_stream"   "nt,d"         weight-streaming kernel shape
+ *   "lmhead_rows"     "nt,nw,d"      shared-activation streaming kernel shape
+ *   "lmhead_decode"   "nt,d"         register-staged decode kernel shape
+ *   "lmhead_kouter"   "0" (never) or "nt,nw,d,tmax" (only that shape)
+ *   "lmhead_gemm"     "n"            compute-regime kernel variant (0 automatic)
+ *   "draft_tail"      "split" (one row runs as two launches, not fused)
+ *   "device_cus"      "n"            size persistent grids for n CUs
+ *
+ * A NULL value clears that key; a NULL key clears every key.  Returns
+ * MTPD_ERR_SHAPE (and changes nothing) for an unknown key or a value that
+ * does not parse.
+ */
+mtpd_status mtpd_set_plan_override(const char *key, const char *value);
 
 /* ABI version: bumped when any declaration above changes. */
 int mtpd_abi_version(void);

@@ -36,7 +36,7 @@ import torch
 __all__ = [
     "MtpdError", "MtpdLibraryMissing", "norm_quant", "fp8_lmhead_argmax", "draft_tail",
     "workspace_bytes", "Workspace", "library_path", "lib", "lmhead_plan", "draft_tail_plan",
-    "allreduce_norm_quant", "argmax_combine", "fp8_lmhead_topk", "topk_workspace_bytes",
+    "allreduce_norm_quant", "argmax_combine", "fp8_lmhead_topk", "topk_workspace_bytes", "plan_override",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -119,6 +119,8 @@ def lib():
         L.mtpd_draft_tail_plan.argtypes = [I64, I64, I64]
         L.mtpd_abi_version.restype = ctypes.c_int
         L.mtpd_abi_version.argtypes = []
+        L.mtpd_set_plan_override.restype = ctypes.c_int
+        L.mtpd_set_plan_override.argtypes = [ctypes.c_char_p, ctypes.c_char_p]
         _lib = L
         return L
 
@@ -150,19 +152,41 @@ class Workspace:
     """A zero-filled device workspace, grown on demand and reused.
 
     The library leaves the workspace zero-filled after every completed call,
-    so one buffer serves any number of calls issued in order on one stream.
+    so one buffer serves any number of calls issued in order on ONE stream:
+    calls in flight together on two streams would merge their argmax keys and
+    arrival counters.  The workspace therefore binds to the stream of its
+    first call and raises ValueError if a later call runs on another stream
+    (the default workspaces are kept per device and stream, so they never
+    do).  ``any_stream=True`` lifts the check for callers that order every
+    use themselves, e.g. a HIP graph captured on torch's capture stream and
+    replayed on the stream of the eager calls.  When the buffer grows, the
+    old one is released only after the work already queued on the stream of
+    its last use (``record_stream``).
     """
 
-    def __init__(self, device=None):
+    def __init__(self, device=None, any_stream: bool = False):
         self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
         self.buf = None
+        self.stream = None
+        self.any_stream = bool(any_stream)
 
     def get(self, n_rows: int) -> torch.Tensor:
         return self.get_bytes(workspace_bytes(n_rows))
 
     def get_bytes(self, need: int) -> torch.Tensor:
+        stream = torch.cuda.current_stream(self.device)
+        if self.stream is None or self.any_stream:
+            if self.buf is not None and self.stream is not None and self.stream.cuda_stream != stream.cuda_stream:
+                self.buf.record_stream(stream)
+            self.stream = stream
+        elif self.stream.cuda_stream != stream.cuda_stream:
+            raise ValueError("this Workspace is bound to another stream; calls that may overlap in time "
+                             "need separate workspaces")
         if self.buf is None or self.buf.numel() < need:
-            self.buf = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.device)
+            if self.buf is not None:
+                self.buf.record_stream(self.stream)
+            with torch.cuda.stream(self.stream):
+                self.buf = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.device)
         return self.buf
 
 
@@ -170,7 +194,7 @@ _default_ws: dict = {}
 
 
 def _workspace_for(device: torch.device) -> Workspace:
-    key = (device.type, device.index)
+    key = (device.type, device.index, torch.cuda.current_stream(device).cuda_stream)
     if key not in _default_ws:
         _default_ws[key] = Workspace(device)
     return _default_ws[key]
@@ -178,6 +202,42 @@ def _workspace_for(device: torch.device) -> Workspace:
 
 def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
+
+
+_OVERRIDE_KEYS = ("lmhead_kernel", "lmhead_tile", "lmhead_stream", "lmhead_rows", "lmhead_decode",
+                  "lmhead_kouter", "lmhead_gemm", "draft_tail", "device_cus")
+
+
+class plan_override:
+    """Context manager pinning the library's launch plan (tuning and tests only).
+
+    ``with plan_override(lmhead_kernel="generic", device_cus=8): ...`` sets the
+    given keys of ``mtpd_set_plan_override`` (values as strings, tuples or
+    ints; None leaves a key automatic) and clears every key on exit.  The
+    setting is process-wide: use it only while no other thread calls the
+    library.
+    """
+
+    def __init__(self, **keys):
+        for k in keys:
+            if k not in _OVERRIDE_KEYS:
+                raise KeyError(f"unknown plan-override key {k!r}")
+        self.keys = keys
+
+    def __enter__(self):
+        L = lib()
+        L.mtpd_set_plan_override(None, None)
+        for k, v in self.keys.items():
+            if v is None:
+                continue
+            if isinstance(v, (tuple, list)):
+                v = ",".join(str(int(x)) for x in v)
+            _check(L.mtpd_set_plan_override(k.encode(), str(v).encode()))
+        return self
+
+    def __exit__(self, *exc):
+        lib().mtpd_set_plan_override(None, None)
+        return False
 
 
 def _dev(t: torch.Tensor, name: str, dtypes, dim: int):
@@ -356,7 +416,7 @@ def fp8_lmhead_topk(codes, scales, w_codes, w_scales, k: int, row_index=None, wo
     Returns (values float32 [n, k], idx int32 [n, k]), each row in descending
     order of the fp32 logit, equal values in ascending index order.  The
     workspace holds candidate lists and needs no zeroing; by default one
-    buffer per device (separate from the argmax workspace) is reused.
+    buffer per device and stream (separate from the argmax workspace) is reused.
     """
     _dev(codes, "codes", _U8, 2)
     _dev(scales, "scales", (torch.float32,), 2)
@@ -376,7 +436,7 @@ def fp8_lmhead_topk(codes, scales, w_codes, w_scales, k: int, row_index=None, wo
     else:
         out_val, out_idx = out
     if workspace is None:
-        key = (dev.type, dev.index)
+        key = (dev.type, dev.index, torch.cuda.current_stream(dev).cuda_stream)
         if key not in _topk_ws:
             _topk_ws[key] = Workspace(dev)
         workspace = _topk_ws[key]

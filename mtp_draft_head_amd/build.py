@@ -30,8 +30,17 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
 EXTRA = {"lmhead_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
+# measured-peak probes (a streaming read and an FP8 MFMA loop) used by the
+# benchmark's roofline; a library of their own, never linked into libmtpd
+PEAK_SOURCES = ["peak_probe.hip"]
+
+
 def library_path() -> str:
     return os.path.join(OUT_DIR, "libmtpd.so")
+
+
+def peaks_library_path() -> str:
+    return os.path.join(OUT_DIR, "libmtpd_peaks.so")
 
 
 def _compile(src: str, verbose: bool) -> str:
@@ -45,11 +54,7 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    out = library_path()
+def _link(objs, out: str, verbose: bool) -> str:
     tmp = out + f".tmp{os.getpid()}"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
@@ -57,6 +62,15 @@ def build(verbose: bool = False) -> str:
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    srcs = SOURCES + PEAK_SOURCES
+    with ThreadPoolExecutor(len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in PEAK_SOURCES], peaks_library_path(), verbose)
+    return _link([objs[s] for s in SOURCES], library_path(), verbose)
 
 
 if __name__ == "__main__":

@@ -57,8 +57,9 @@ hipError_t launch_lmhead_argmax(const LmheadArgs& a, hipStream_t stream);
 // name and launch shape of the kernel launch_lmhead_argmax picks
 void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len);
 
-// the compute-regime kernel (lmhead_gemm.hip): 256 x 256 tiles, V % 256 == 0
+// the compute-regime kernels (lmhead_gemm.hip): 256-column tiles, V % 256 == 0
 hipError_t launch_lmhead_gemm(const LmheadArgs& a, hipStream_t stream);
+void describe_gemm(int64_t n_rows, int64_t V, int64_t H, int64_t a_rows, char* buf, size_t len);
 
 // the weight-streaming kernel for one row tile (lmhead_stream.hip): n_rows <= 16
 bool stream_config_compiled(int nt, int ma, int d);
@@ -78,8 +79,26 @@ bool kouter_choose(int mt, int64_t V, int cus, KouterTile* out);
 hipError_t launch_lmhead_kouter(const LmheadArgs& a, int mt, int nt, int nw, int d, int tmax, int cus,
                                 hipStream_t stream);
 
-// multiprocessor count of the current device (cached per device)
+// multiprocessor count of the current device (cached per device), or the
+// plan override's count
 int device_cus();
+
+// Launch-plan overrides for tuning sweeps and tests, written only by
+// mtpd_set_plan_override (all zero: the dispatcher chooses).  Process-wide;
+// read by the host-side dispatch of every call.
+struct PlanOverride {
+    int lmhead_kernel;       // 0 auto; 1 the generic tiled kernel only; 2 no streaming kernels (decode or generic)
+    int tile[3];             // generic kernel nt, s, d
+    int stream[2];           // weight-streaming kernel nt, d
+    int rows[3];             // shared-activation streaming kernel nt, nw, d
+    int decode[2];           // register-staged decode kernel nt, d
+    int kouter;              // 0 auto; -1 never; 1 only the shape in kouter_shape
+    int kouter_shape[4];     // nt, nw, d, tmax
+    int draft_tail_split;    // 1: one row runs norm_quant + the LM head, not the fused tail
+    int device_cus;          // > 0: persistent grids sized as if the device had this many CUs
+    int gemm;                // 0 auto; otherwise a compute-regime kernel variant (lmhead_gemm.hip)
+};
+const PlanOverride& plan_override();
 
 // top-k of the LM head (lmhead_stream.hip): at most 64 rows per call, k <= 32;
 // workspace: the candidate lists (no zeroing needed)

@@ -250,12 +250,9 @@ __global__ __launch_bounds__(64 * S) void lmhead_argmax_kernel(
 }
 
 int device_cus() {
-    // "MTPD_DEVICE_CUS=n" sizes the persistent grids as if the device had n
+    // the override sizes the persistent grids as if the device had that many
     // CUs (testing: several tiles per workgroup at small vocab sizes)
-    if (const char* e = getenv("MTPD_DEVICE_CUS")) {
-        const int n = atoi(e);
-        if (n > 0) return n;
-    }
+    if (plan_override().device_cus > 0) return plan_override().device_cus;
     static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -310,10 +307,10 @@ Tile choose_tile(int64_t n_rows, int64_t V, int64_t H) {
     t.s = 1;
     if (t.mt == 1) t.d = 4;
     while (t.s < 4 && tiles * t.s < want_waves / 4 && 2 * t.s * t.d <= KB) t.s *= 2;
-    // optional launch-shape override for tuning sweeps: MTPD_LMHEAD_TILE="nt,s,d"
-    if (const char* e = getenv("MTPD_LMHEAD_TILE")) {
-        Tile o = t;
-        if (sscanf(e, "%d,%d,%d", &o.nt, &o.s, &o.d) == 3 && compiled(o)) t = o;
+    // optional launch-shape override (tuning sweeps, tests)
+    if (const int* o = plan_override().tile; o[0] > 0) {
+        const Tile ot{t.mt, o[0], o[1], o[2]};
+        if (compiled(ot)) t = ot;
     }
     while (!compiled(t) || lds_bytes(t, KB) > 64 * 1024) {
         if (t.s > 1) t.s /= 2;
@@ -354,10 +351,7 @@ bool choose_decode(int64_t n_rows, int64_t V, int64_t H, DecodeTile* out) {
     const int mt = n_rows <= 16 ? 1 : (n_rows <= 32 ? 2 : 4);
     DecodeTile cand[6];
     int nc = 0;
-    if (const char* e = getenv("MTPD_LMHEAD_DECODE")) {   // tuning override "nt,d"
-        DecodeTile o{mt, 0, 0};
-        if (sscanf(e, "%d,%d", &o.nt, &o.d) == 2) cand[nc++] = o;
-    }
+    if (const int* o = plan_override().decode; o[0] > 0) cand[nc++] = DecodeTile{mt, o[0], o[1]};   // tuning
     if (mt == 1) {
         cand[nc++] = {1, 1, 8};
         cand[nc++] = {1, 1, 4};
@@ -387,19 +381,15 @@ struct StreamTile {
 
 // Up to 16 rows and H <= stream_max_h(): the weight-streaming kernel, if a
 // compiled (NT, MA, D) fits (16*NT must divide V; MA eight-row activation
-// pieces; activation offsets are 32-bit).  "MTPD_LMHEAD_STREAM=nt,d"
-// overrides NT and D (tuning).
+// pieces; activation offsets are 32-bit).  The plan override's stream shape
+// replaces NT and D (tuning).
 bool use_stream(int64_t n_rows, int64_t V, int64_t H, int64_t a_rows, StreamTile* out) {
-    const char* kind = getenv("MTPD_LMHEAD_KERNEL");
-    if (kind && strcmp(kind, "generic") == 0) return false;
+    if (plan_override().lmhead_kernel != 0) return false;
     if (n_rows < 1 || n_rows > 16 || H > stream_max_h() || a_rows * H > ((int64_t)1 << 32)) return false;
     const int ma = n_rows <= 8 ? 1 : 2;
     StreamTile cand[3];
     int nc = 0;
-    if (const char* e = getenv("MTPD_LMHEAD_STREAM")) {
-        StreamTile o{0, ma, 0};
-        if (sscanf(e, "%d,%d", &o.nt, &o.d) == 2) cand[nc++] = o;
-    }
+    if (const int* o = plan_override().stream; o[0] > 0) cand[nc++] = StreamTile{o[0], ma, o[1]};
     cand[nc++] = {1, ma, 8};
     cand[nc++] = {1, ma, 4};
     for (int i = 0; i < nc; ++i) {
@@ -417,18 +407,14 @@ struct RowsTile {
 
 // 17..64 rows, H <= stream_max_h(), 32-bit activation offsets: the streaming
 // kernel with a shared activation ring, if a compiled (MT, NT, NW, D) fits
-// (16*NT*NW must divide V).  "MTPD_LMHEAD_ROWS=nt,nw,d" overrides (tuning).
+// (16*NT*NW must divide V).  The plan override's rows shape comes first (tuning).
 bool use_rows(int64_t n_rows, int64_t V, int64_t H, int64_t a_rows, RowsTile* out) {
-    const char* kind = getenv("MTPD_LMHEAD_KERNEL");
-    if (kind && (strcmp(kind, "generic") == 0 || strcmp(kind, "decode") == 0)) return false;
+    if (plan_override().lmhead_kernel != 0) return false;
     if (n_rows <= 16 || n_rows > 64 || H > stream_max_h() || a_rows * H > ((int64_t)1 << 32)) return false;
     const int mt = n_rows <= 32 ? 2 : 4;
     RowsTile cand[4];
     int nc = 0;
-    if (const char* e = getenv("MTPD_LMHEAD_ROWS")) {
-        RowsTile o{mt, 0, 0, 0};
-        if (sscanf(e, "%d,%d,%d", &o.nt, &o.nw, &o.d) == 3) cand[nc++] = o;
-    }
+    if (const int* o = plan_override().rows; o[0] > 0) cand[nc++] = RowsTile{mt, o[0], o[1], o[2], {}};
     if (mt == 4) {
         cand[nc++] = {4, 2, 4, 5};
         cand[nc++] = {4, 1, 4, 6};
@@ -449,22 +435,21 @@ bool use_rows(int64_t n_rows, int64_t V, int64_t H, int64_t a_rows, RowsTile* ou
 }
 
 bool use_decode(int64_t n_rows, int64_t V, int64_t H, DecodeTile* dt) {
-    const char* kind = getenv("MTPD_LMHEAD_KERNEL");   // "generic" forces the tiled kernel (testing)
-    return !(kind && strcmp(kind, "generic") == 0) && choose_decode(n_rows, V, H, dt);
+    // the override's "generic" forces the tiled kernel (testing)
+    return plan_override().lmhead_kernel != 1 && choose_decode(n_rows, V, H, dt);
 }
 
 // many rows: the LDS-tiled 256 x 256 kernel
 // The tiled kernel addresses the activation with 32-bit byte offsets.
 bool use_gemm(int64_t n_rows, int64_t V, int64_t H, int64_t a_rows) {
-    const char* kind = getenv("MTPD_LMHEAD_KERNEL");
-    if (kind && strcmp(kind, "generic") == 0) return false;
+    if (plan_override().lmhead_kernel == 1) return false;
     return n_rows > 64 && V % 256 == 0 && a_rows * H <= ((int64_t)1 << 32);
 }
 
 void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len) {
     DecodeTile dt;
     if (use_gemm(n_rows, V, H, n_rows)) {
-        snprintf(buf, len, "lmhead_gemm_kernel grid=%lldx512", (long long)((n_rows + 255) / 256 * (V / 256)));
+        describe_gemm(n_rows, V, H, n_rows, buf, len);
         return;
     }
     StreamTile st;

@@ -30,6 +30,10 @@
 //    merge per row into the partitioned key slots, arrival, and the last
 //    workgroup decodes (lmhead_common.h).
 
+#include <stdio.h>
+
+#include <algorithm>
+
 #include "kernels.h"
 #include "lmhead_common.h"
 
@@ -282,7 +286,475 @@ __global__ __launch_bounds__(512) void lmhead_gemm_kernel(
     finalize_argmax<512>(ws, n_rows, out_max, out_idx, red);
 }
 
+
+// ---------------------------------------------------------------------------
+// Pipelined form: the same tile algebra with the LDS fragment reads issued
+// from inline asm and their waits placed by hand.
+//
+//  - BM = 32 * MT activation rows x 256 vocab rows per workgroup (8 waves,
+//    2 x 4, each 16 * MT rows x 64 columns).  MT = 8 gives 256-row tiles;
+//    MT = 5 gives 160-row tiles, whose height divides 320 rows exactly.
+//  - Staging: per K block both operand tiles go global -> LDS as [row][128
+//    bytes], eight consecutive lanes per row's 128 bytes (a whole cache line
+//    per eight lanes: measured 12.4 against 10.7 TB/s of L2 -> LDS for four
+//    lanes per 64-byte half, copies alone, every CU busy), chunk c of row r
+//    at position c ^ ((r >> 1) & 7).
+//  - MFMA lane l supplies row l % 16 and, for its 32 K bytes, 16-byte chunks
+//    l / 16 and l / 16 + 4 of that row (A and B permute K the same way, so
+//    the dot product is unchanged): each of the two fragment reads then
+//    touches 16 rows at one chunk each, and the swizzle spreads any 16
+//    consecutive lanes over all 64 banks.
+//  - Block scales: the activation scales of block kb + 1 travel with the
+//    codes of block kb; during block kb every thread forms one entry
+//    sa[row] * sw[block] of block kb + 1's scale table (2 weight-scale
+//    blocks x BM rows), so the promotion reads its factors instead of
+//    multiplying them per wave.
+//  - Per K block a wave issues its first row group's activation fragment and
+//    factors and its four weight fragments, then starts each of the first
+//    group's MFMAs as soon as that MFMA's own operands have arrived (reads
+//    return in issue order, so partial counts suffice); later groups wait
+//    only for what the previous group issued.  The compiler's own waits
+//    drained every read, the one just issued included.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int MT>
+struct G2 {
+    static constexpr int BM = 32 * MT;                // activation rows per tile
+    static constexpr int A_BYTES = BM * 128;          // activation tile, [row][128 bytes]
+    static constexpr int W_BYTES = 256 * 128;         // weight tile
+    static constexpr int SA_FLOATS = (BM + 63) / 64 * 64;
+    // LDS, operand-major so that one base register per fragment half reaches
+    // both stages through the 16-bit immediate offset: [A stage 0][A stage 1]
+    // [W stage 0][W stage 1][scales stage 0][scales stage 1]
+    static constexpr int W_OFF = 2 * A_BYTES;
+    static constexpr int SA_OFF = W_OFF + 2 * W_BYTES;
+    static constexpr int SMEM = SA_OFF + 2 * SA_FLOATS * 4;
+    static constexpr int A_COPIES = BM / 8;           // copies of 8 rows x 128 bytes
+    static constexpr int SCOPY = SA_FLOATS / 64;      // scale copies of 64 rows
+    static constexpr int SW_MAX = 64;                 // K blocks of the weight-scale table (H <= 8192)
+    static_assert(A_BYTES + 7 * 2048 < 65536 && W_BYTES + 6 * 2048 < 65536, "immediate offsets");
+};
+
+// position of 16-byte chunk c of row r inside the row's 128 bytes
+__device__ __forceinline__ int chunk_pos(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+template <int OFF>
+__device__ __forceinline__ u32x4_t lds_read16_off(uint32_t addr) {
+    u32x4_t v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+
+// lds_read16_off<s * SBYTES + k * STEP>(addr) for a stage s (0, 1) and a k
+// (0..7) known after unrolling
+template <int SBYTES, int STEP>
+__device__ __forceinline__ u32x4_t lds_read16_sk(uint32_t addr, int s, int k) {
+#define MTPD_CASE(S, K) \
+    case S * 8 + K: return lds_read16_off<S * SBYTES + K * STEP>(addr);
+    switch (s * 8 + k) {
+        MTPD_CASE(0, 0) MTPD_CASE(0, 1) MTPD_CASE(0, 2) MTPD_CASE(0, 3)
+        MTPD_CASE(0, 4) MTPD_CASE(0, 5) MTPD_CASE(0, 6) MTPD_CASE(0, 7)
+        MTPD_CASE(1, 0) MTPD_CASE(1, 1) MTPD_CASE(1, 2) MTPD_CASE(1, 3)
+        MTPD_CASE(1, 4) MTPD_CASE(1, 5) MTPD_CASE(1, 6)
+        default: return lds_read16_off<SBYTES + 7 * STEP>(addr);
+    }
+#undef MTPD_CASE
+}
+
+__device__ __forceinline__ v8i frag_of(u32x4_t lo, u32x4_t hi) {
+    v8i f;
+    f[0] = (int)lo[0]; f[1] = (int)lo[1]; f[2] = (int)lo[2]; f[3] = (int)lo[3];
+    f[4] = (int)hi[0]; f[5] = (int)hi[1]; f[6] = (int)hi[2]; f[7] = (int)hi[3];
+    return f;
+}
+
+// Waits until at most N LDS reads of this wave are outstanding (reads return
+// in issue order); the registers those reads fill are tied to the wait, so no
+// use of them is scheduled above it.  (Inline asm and device builtins live in
+// device functions only: a kernel template whose own body holds them fails
+// to instantiate in the host pass, and its launch stub is not emitted.)
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b) {
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b, u32x4_t& c) {
+    asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(a), "+v"(b), "+v"(c) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b, u32x4_t& c, u32x4_t& d, u32x4_t& e) {
+    asm volatile("s_waitcnt lgkmcnt(%5)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e) : "n"(N));
+}
+
+// 1 if the predicate holds on any lane of the wave
+__device__ __forceinline__ unsigned int any_lane(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0 ? 1u : 0u; }
+
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// scheduling fence: nothing moves across it
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// workgroup barrier after this wave's LDS accesses (the scale-table writes)
+// and LDS-DMA copies have completed
+__device__ __forceinline__ void drain_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// direct global -> LDS copies of 16 (4) bytes per lane, lane i's bytes to lds + i * 16 (4)
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds, 4, 0, 0);
+}
+
+// The same copies through a raw buffer resource: a 32-bit per-lane byte
+// offset plus a wave-uniform one, no 64-bit address arithmetic per copy
+// (the global form's per-copy address pairs, hoisted out of the K loop, ran
+// the register file out).  Third descriptor word: 32-bit data format, the
+// raw-buffer setting of this architecture family.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ void bdma16(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void bdma4(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
+}
+
+// hides a value from constant folding (the zero accumulators of the first block)
+__device__ __forceinline__ void opaque(float& x) { asm volatile("" : "+v"(x)); }
+
+}  // namespace
+
+template <int MT>
+__global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
+    const uint8_t* __restrict__ a_codes, const float* __restrict__ a_scales,
+    const int32_t* __restrict__ row_index, int n_rows,
+    const uint8_t* __restrict__ w_codes, const float* __restrict__ w_scales, int H,
+    int n_row_tiles, int n_col_tiles, int group_rows,
+    float* __restrict__ out_max, int32_t* __restrict__ out_idx, ArgmaxWs ws)
+{
+    using C = G2<MT>;
+    constexpr int BM = C::BM;
+    static_assert(C::SMEM + 2 * 2 * BM * 4 + 2 * C::SW_MAX * 4 <= 160 * 1024, "LDS");
+    static_assert(4 * BM * 8 <= C::SMEM, "epilogue table must fit in the stage memory");
+    __shared__ __align__(16) unsigned char smem[C::SMEM];
+    __shared__ __align__(16) float ftab[2][2][BM];        // [slot][weight-scale block][row] promotion factors
+    __shared__ __align__(16) float swtab[2][C::SW_MAX];   // weight scales of the tile's two 128-row blocks
+    __shared__ unsigned int deps[8];
+    __shared__ int last_flag;
+
+    const int KB = H >> 7;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = wave_uniform(t >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+
+    // tile order: row tiles in groups of group_rows, row fastest inside a
+    // group, then column; consecutive ids run together on one XCD
+    const int total = n_row_tiles * n_col_tiles;
+    const int id = xcd_contiguous((int)blockIdx.x, total);
+    const int group_tiles = group_rows * n_col_tiles;
+    const int grp = id / group_tiles;
+    const int rows_in_grp = min(group_rows, n_row_tiles - grp * group_rows);
+    const int in_grp = id - grp * group_tiles;
+    const int rt = grp * group_rows + in_grp % rows_in_grp;
+    const int ct = in_grp / rows_in_grp;
+    const int m0 = rt * BM, n0 = ct * 256;
+
+    // ---- copy assignment (global -> LDS, no VGPRs) ----
+    // Copy j of an operand moves rows 8j .. 8j + 7: lane i lands at position
+    // i & 7 of row 8j + (i >> 3), so it reads the chunk stored there.
+    // Activation copies j = wave, wave + 8, ... (rows past n_rows repeat its
+    // last row); weight copies 4 * wave .. 4 * wave + 3; scale copy `wave` on
+    // the first SCOPY waves (64 rows; rows past the tile repeat its last row).
+    // Offsets are 32-bit from wave-uniform bases (the host keeps the
+    // activation and its scales under 2 GiB for this kernel).
+    const int crow = lane >> 3;
+    constexpr int AC = (C::A_COPIES + 7) / 8;
+    uint32_t aoff[AC], woff[4];
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+        const int j = min(wave + 8 * i, C::A_COPIES - 1);
+        const int r = j * 8 + crow;
+        const int m = min(m0 + r, n_rows - 1);
+        const uint32_t a = (uint32_t)(row_index ? row_index[m] : m);
+        aoff[i] = a * (uint32_t)H + (uint32_t)chunk_pos(r, lane & 7) * 16u;   // chunk_pos is its own inverse in c
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = (4 * wave + i) * 8 + crow;
+        woff[i] = (uint32_t)r * (uint32_t)H + (uint32_t)chunk_pos(r, lane & 7) * 16u;
+    }
+    const rsrc_t a_rs = make_rsrc(a_codes);
+    const rsrc_t w_rs = make_rsrc(w_codes + (size_t)n0 * (size_t)H);
+    const rsrc_t s_rs = make_rsrc(a_scales);
+    const int sa_row = min(m0 + min(wave * 64 + lane, BM - 1), n_rows - 1);
+    const uint32_t saoff = (uint32_t)(row_index ? row_index[sa_row] : sa_row) * (uint32_t)KB * 4u;
+
+    // codes of block kb and activation scales of block skb into stage s
+    auto copy_in = [&](int s, int kb, int skb) {
+        const uint32_t kofs = (uint32_t)kb * kBlock;
+#pragma unroll
+        for (int i = 0; i < AC; ++i) {
+            const int j = wave + 8 * i;
+            if (j < C::A_COPIES) bdma16(a_rs, aoff[i], kofs, smem + s * C::A_BYTES + j * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            bdma16(w_rs, woff[i], kofs, smem + C::W_OFF + s * C::W_BYTES + (4 * wave + i) * 1024);
+        if (wave < C::SCOPY)
+            bdma4(s_rs, saoff, (uint32_t)skb * 4u, smem + C::SA_OFF + s * C::SA_FLOATS * 4 + wave * 256);
+    };
+
+    // ---- fragment addresses (bytes in LDS), one set per stage ----
+    const int fr = lane & 15, fg = lane >> 4;
+    const uint32_t lo16 = (uint32_t)(fr * 128 + chunk_pos(fr, fg) * 16);
+    const uint32_t hi16 = (uint32_t)(fr * 128 + chunk_pos(fr, fg + 4) * 16);
+    const uint32_t smem0 = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
+    const uint32_t a_lo = smem0 + (uint32_t)(wm * MT * 16 * 128) + lo16;
+    const uint32_t a_hi = smem0 + (uint32_t)(wm * MT * 16 * 128) + hi16;
+    const uint32_t b_lo = smem0 + (uint32_t)(C::W_OFF + wn * 64 * 128) + lo16;
+    const uint32_t b_hi = smem0 + (uint32_t)(C::W_OFF + wn * 64 * 128) + hi16;
+    const uint32_t f_ad = (uint32_t)(uintptr_t)(lds_ptr_t)&ftab[0][wn >> 1][wm * MT * 16 + 4 * fg];
+    constexpr int FSLOT = 2 * BM * 4;   // bytes between the two factor slots
+
+    float acc[MT][4][4];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) opaque(acc[i][j][r]);
+
+    v4f ring[2];        // the last two MFMA results, each folded in one MFMA later
+    u32x4_t fv[2];      // promotion factors of a row group's four rows (by group parity)
+
+    // (each updated accumulator passes through an empty asm, so the FMA stays
+    // where it is written: left alone, the compiler sinks every fold-in of a
+    // block past the block's barrier, keeping all its MFMA results live)
+    auto promote = [&](int mt, int nt, const v4f& p, const u32x4_t& f) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            acc[mt][nt][r] = fmaf(p[r], __uint_as_float(f[r]), acc[mt][nt][r]);
+            opaque(acc[mt][nt][r]);
+        }
+    };
+
+    // One K block from stage s, factor slot s.  MFMA (g, nt) -> ring[n % 2]
+    // (n its index in the block); its fold-in follows the next MFMA, so the
+    // matrix result is ready by then and the other wave fills the gap.  Read
+    // order: group g + 1's activation and factors are issued after group g's
+    // first MFMA and the fold-in of group g - 1's last one (which frees the
+    // factor slot); the block's first batch is group 0's and all four weight
+    // fragments, and group 0's MFMAs start as their own operands arrive.
+    auto compute = [&](int s) {
+        u32x4_t alo[2], ahi[2];
+        alo[0] = lds_read16_sk<C::A_BYTES, 2048>(a_lo, s, 0);
+        ahi[0] = lds_read16_sk<C::A_BYTES, 2048>(a_hi, s, 0);
+        fv[0] = lds_read16_sk<FSLOT, 64>(f_ad, s, 0);
+        u32x4_t b0 = lds_read16_sk<C::W_BYTES, 2048>(b_lo, s, 0), b1 = lds_read16_sk<C::W_BYTES, 2048>(b_hi, s, 0);
+        u32x4_t b2 = lds_read16_sk<C::W_BYTES, 2048>(b_lo, s, 1), b3 = lds_read16_sk<C::W_BYTES, 2048>(b_hi, s, 1);
+        u32x4_t b4 = lds_read16_sk<C::W_BYTES, 2048>(b_lo, s, 2), b5 = lds_read16_sk<C::W_BYTES, 2048>(b_hi, s, 2);
+        u32x4_t b6 = lds_read16_sk<C::W_BYTES, 2048>(b_lo, s, 3), b7 = lds_read16_sk<C::W_BYTES, 2048>(b_hi, s, 3);
+        v8i bf[4];
+        // in flight: A0 (2), F0, B0 .. B3 (8): the first 5 are group 0's and B0
+        lds_wait<6>(alo[0], ahi[0], fv[0], b0, b1);
+        const v8i af0 = frag_of(alo[0], ahi[0]);
+        bf[0] = frag_of(b0, b1);
+        sched_fence();
+        ring[0] = mfma_e4m3(af0, bf[0]);
+        if (MT > 1) {
+            alo[1] = lds_read16_sk<C::A_BYTES, 2048>(a_lo, s, 1);
+            ahi[1] = lds_read16_sk<C::A_BYTES, 2048>(a_hi, s, 1);
+            fv[1] = lds_read16_sk<FSLOT, 64>(f_ad, s, 1);
+        }
+        sched_fence();
+        // in flight: B1 .. B3 (6), then group 1's 3
+        constexpr int NXT = MT > 1 ? 3 : 0;
+        lds_wait<NXT + 4>(b2, b3);
+        bf[1] = frag_of(b2, b3);
+        ring[1] = mfma_e4m3(af0, bf[1]);
+        sched_fence();   // the MFMA issues first, then the previous one's fold-in
+        promote(0, 0, ring[0], fv[0]);
+        sched_fence();
+        lds_wait<NXT + 2>(b4, b5);
+        bf[2] = frag_of(b4, b5);
+        ring[0] = mfma_e4m3(af0, bf[2]);
+        sched_fence();
+        promote(0, 1, ring[1], fv[0]);
+        sched_fence();
+        lds_wait<NXT>(b6, b7);
+        bf[3] = frag_of(b6, b7);
+        ring[1] = mfma_e4m3(af0, bf[3]);
+        sched_fence();
+        promote(0, 2, ring[0], fv[0]);
+        sched_fence();
+#pragma unroll
+        for (int mt = 1; mt < MT; ++mt) {
+            const int slot = mt & 1;
+            lds_wait<0>(alo[slot], ahi[slot], fv[slot]);
+            const v8i af = frag_of(alo[slot], ahi[slot]);
+            ring[0] = mfma_e4m3(af, bf[0]);
+            sched_fence();
+            promote(mt - 1, 3, ring[1], fv[slot ^ 1]);
+            if (mt + 1 < MT) {
+                alo[slot ^ 1] = lds_read16_sk<C::A_BYTES, 2048>(a_lo, s, mt + 1);
+                ahi[slot ^ 1] = lds_read16_sk<C::A_BYTES, 2048>(a_hi, s, mt + 1);
+                fv[slot ^ 1] = lds_read16_sk<FSLOT, 64>(f_ad, s, mt + 1);
+            }
+            sched_fence();
+            ring[1] = mfma_e4m3(af, bf[1]);
+            sched_fence();
+            promote(mt, 0, ring[0], fv[slot]);
+            sched_fence();
+            ring[0] = mfma_e4m3(af, bf[2]);
+            sched_fence();
+            promote(mt, 1, ring[1], fv[slot]);
+            sched_fence();
+            ring[1] = mfma_e4m3(af, bf[3]);
+            sched_fence();
+            promote(mt, 2, ring[0], fv[slot]);
+            sched_fence();
+        }
+        promote(MT - 1, 3, ring[1], fv[(MT - 1) & 1]);
+    };
+
+    // promotion factors of block kb from the activation scales in a stage
+    // (thread t: weight-scale block t / BM, row t % BM)
+    auto factors = [&](int slot, int s, int kb) {
+        for (int e = t; e < 2 * BM; e += 512) {
+            const int cb = e / BM, r = e - cb * BM;
+            const float sa = reinterpret_cast<const float*>(smem + C::SA_OFF + s * C::SA_FLOATS * 4)[r];
+            ftab[slot][cb][r] = sa * swtab[cb][kb];
+        }
+    };
+
+    // ---- pipeline ----
+    // Prologue: the weight-scale table, block 0's activation scales (into
+    // stage 1's scale slot, idle until block 1's copy), stage 0 = codes of
+    // block 0 with the scales of block 1; then block 0's factors.
+    // Block kb computes from stage kb % 2 and factor slot kb % 2, while the
+    // copy of block kb + 1 (with the scales of block kb + 2) fills the other
+    // stage and every thread forms one factor of block kb + 1 from the scales
+    // stage kb holds; the barrier ending the block publishes both.
+    if (wave < 2)
+        dma4(w_scales + (size_t)((n0 >> 7) + wave) * KB + min(lane, KB - 1), &swtab[wave][0]);
+    if (wave < C::SCOPY) bdma4(s_rs, saoff, 0u, smem + C::SA_OFF + C::SA_FLOATS * 4 + wave * 256);
+    copy_in(0, 0, min(1, KB - 1));
+    drain_barrier();
+    factors(0, 1, 0);
+    drain_barrier();
+    for (int kb = 0; kb < KB; kb += 2) {
+        // stage 0
+        if (kb + 1 < KB) copy_in(1, kb + 1, min(kb + 2, KB - 1));
+        compute(0);
+        if (kb + 1 < KB) factors(1, 0, kb + 1);
+        drain_barrier();
+        if (kb + 1 >= KB) break;
+        // stage 1
+        if (kb + 2 < KB) copy_in(0, kb + 2, min(kb + 3, KB - 1));
+        compute(1);
+        if (kb + 2 < KB) factors(0, 1, kb + 2);
+        drain_barrier();
+    }
+
+    // ---- epilogue: per-row best over the wave's 64 columns, then over the
+    // four column waves (table in the now idle stage memory) ----
+    unsigned long long* red = reinterpret_cast<unsigned long long*>(smem);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint64_t best = 0;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                best = u64_max(best, argmax_key(acc[mt][nt][i],
+                                                (uint32_t)(n0 + wn * 64 + nt * 16 + (lane & 15))));
+            best = row16_max_u64(best);
+            if ((lane & 15) == 0) red[wn * BM + wm * MT * 16 + mt * 16 + 4 * (lane >> 4) + i] = best;
+        }
+    }
+    __syncthreads();
+    uint64_t old = 0;
+    if (t < BM && m0 + t < n_rows) {
+        const uint64_t k = u64_max(u64_max(red[t], red[BM + t]), u64_max(red[2 * BM + t], red[3 * BM + t]));
+        old = merge_key(ws, n_rows, id, m0 + t, k);
+    }
+    const unsigned int dep = any_lane(never_nonzero(old) != 0);
+    if (lane == 0) deps[wave] = dep;
+    __syncthreads();
+    if (t == 0) {
+        unsigned int d = 0;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) d |= deps[w];
+        last_flag = arrive(ws, id, total, d) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    finalize_argmax<512>(ws, n_rows, out_max, out_idx, red);
+}
+
+template <int MT>
+hipError_t launch_gemm2(const LmheadArgs& a, int group_rows, hipStream_t stream) {
+    constexpr int BM = 32 * MT;
+    const int64_t row_tiles = (a.n_rows + BM - 1) / BM;
+    const int64_t col_tiles = a.V / 256;
+    if (row_tiles * col_tiles > 0x7FFFFFFF || a.H > 128 * G2<MT>::SW_MAX || a.a_rows * a.H >= ((int64_t)1 << 31))
+        return hipErrorInvalidValue;
+    const int gr = (int)std::max<int64_t>(1, std::min<int64_t>(group_rows, row_tiles));
+    hipLaunchKernelGGL((lmhead_gemm2_kernel<MT>), dim3((unsigned)(row_tiles * col_tiles)), dim3(512), 0, stream,
+                       a.a_codes, a.a_scales, a.row_index, (int)a.n_rows, a.w_codes, a.w_scales, (int)a.H,
+                       (int)row_tiles, (int)col_tiles, gr, a.out_max, a.out_idx, argmax_ws(a.workspace, a.n_rows));
+    return hipGetLastError();
+}
+
+int gemm_variant(int64_t n_rows, int64_t H, int64_t a_rows) {
+    const int o = plan_override().gemm;
+    if (o >= 1 && o <= 6) return o;
+    // the pipelined kernel takes H <= 8192 (its weight-scale table) and an
+    // activation under 2 GiB (32-bit buffer offsets)
+    if (H > 128 * G2<8>::SW_MAX || a_rows * H >= ((int64_t)1 << 31)) return 1;
+    // tile height: fewest copied bytes, row tiles x (tile rows + 256 weight
+    // rows) per K block (320 rows: two 160-row tiles, not two 256-row tiles
+    // of which 192 rows are padding)
+    const int64_t c8 = (n_rows + 255) / 256 * (256 + 256), c5 = (n_rows + 159) / 160 * (160 + 256);
+    return c5 < c8 ? 6 : 3;
+}
+
+void describe_gemm(int64_t n_rows, int64_t V, int64_t H, int64_t a_rows, char* buf, size_t len) {
+    const int v = gemm_variant(n_rows, H, a_rows);
+    const int bm = v == 1 ? 256 : (v <= 4 ? 256 : 160);
+    const long long tiles = (long long)((n_rows + bm - 1) / bm * (V / 256));
+    if (v == 1) snprintf(buf, len, "lmhead_gemm_kernel grid=%lldx512", tiles);
+    else snprintf(buf, len, "lmhead_gemm2_kernel<%d> grid=%lldx512 group=%d", bm / 32, tiles, v == 2 || v == 5 ? 4 : (v == 4 ? 16 : 8));
+}
+
 hipError_t launch_lmhead_gemm(const LmheadArgs& a, hipStream_t stream) {
+    // variant 1: the single-wait kernel; 2..6: pipelined shapes
+    switch (gemm_variant(a.n_rows, a.H, a.a_rows)) {
+        case 2: return launch_gemm2<8>(a, 4, stream);
+        case 3: return launch_gemm2<8>(a, 8, stream);
+        case 4: return launch_gemm2<8>(a, 16, stream);
+        case 5: return launch_gemm2<5>(a, 4, stream);
+        case 6: return launch_gemm2<5>(a, 8, stream);
+        default: break;
+    }
     const int64_t row_tiles = (a.n_rows + kBM - 1) / kBM;
     const int64_t col_tiles = a.V / kBN;
     if (row_tiles * col_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;

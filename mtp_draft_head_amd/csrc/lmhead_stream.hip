@@ -988,10 +988,11 @@ __global__ __launch_bounds__(64 * NW) void lmhead_kouter_kernel(
 #define MTPD_KOUTER_CONFIGS(X) X(4, 1, 8, 4, 4) X(4, 2, 4, 5, 5)
 
 bool kouter_choose(int mt, int64_t V, int cus, KouterTile* out) {
-    const char* e = getenv("MTPD_LMHEAD_KOUTER");   // "0": never; "nt,nw,d,tmax": that shape only (testing)
+    // the plan override may rule the kernel out or pin one shape (testing)
+    const PlanOverride& po = plan_override();
     KouterTile want{0, 0, 0, 0};
-    if (e && strcmp(e, "0") == 0) return false;
-    if (e) sscanf(e, "%d,%d,%d,%d", &want.nt, &want.nw, &want.d, &want.tmax);
+    if (po.kouter < 0) return false;
+    if (po.kouter > 0) want = KouterTile{po.kouter_shape[0], po.kouter_shape[1], po.kouter_shape[2], po.kouter_shape[3]};
 #define MTPD_X(a, b2, c2, e2, f)                                                                              \
     if (mt == a && V % (16 * b2 * c2) == 0 && (want.nt == 0 || (want.nt == b2 && want.nw == c2 &&            \
                                                                   want.d == e2 && want.tmax == f))) {        \
@@ -1435,8 +1436,7 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
 }
 
 bool use_draft_tail1(int64_t M, int64_t H) {
-    const char* kind = getenv("MTPD_DRAFT_TAIL");   // "split": norm_quant + LM head (testing)
-    if (kind && strcmp(kind, "split") == 0) return false;
+    if (plan_override().draft_tail_split) return false;   // norm_quant + LM head (testing)
     return M == 1 && H <= kTail1MaxH;
 }
 

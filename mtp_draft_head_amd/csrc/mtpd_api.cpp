@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "kernels.h"
@@ -111,9 +112,88 @@ mtpd_status hip_status(hipError_t e, const char* what) {
     return fail(MTPD_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
 }
 
+mtpd::PlanOverride g_plan{};
+
+// "a,b,c" -> n ints, all positive; false if it does not parse
+bool parse_ints(const char* v, int* out, int n) {
+    int got = 0;
+    const char* p = v;
+    while (got < n) {
+        char* end = nullptr;
+        const long x = strtol(p, &end, 10);
+        if (end == p || x <= 0 || x > 1 << 20) return false;
+        out[got++] = (int)x;
+        if (got < n) {
+            if (*end != ',') return false;
+            p = end + 1;
+        } else if (*end != 0) {
+            return false;
+        }
+    }
+    return true;
+}
+
 }  // namespace
 
+namespace mtpd {
+const PlanOverride& plan_override() { return g_plan; }
+}  // namespace mtpd
+
 extern "C" {
+
+mtpd_status mtpd_set_plan_override(const char* key, const char* value) {
+    if (!key) {
+        g_plan = mtpd::PlanOverride{};
+        return MTPD_OK;
+    }
+    mtpd::PlanOverride p = g_plan;
+    const bool clear = value == nullptr;
+    bool ok = true;
+    if (!strcmp(key, "lmhead_kernel")) {
+        if (clear) p.lmhead_kernel = 0;
+        else if (!strcmp(value, "generic")) p.lmhead_kernel = 1;
+        else if (!strcmp(value, "decode")) p.lmhead_kernel = 2;
+        else ok = false;
+    } else if (!strcmp(key, "lmhead_tile")) {
+        int v[3] = {0, 0, 0};
+        ok = clear || parse_ints(value, v, 3);
+        memcpy(p.tile, v, sizeof v);
+    } else if (!strcmp(key, "lmhead_stream")) {
+        int v[2] = {0, 0};
+        ok = clear || parse_ints(value, v, 2);
+        memcpy(p.stream, v, sizeof v);
+    } else if (!strcmp(key, "lmhead_rows")) {
+        int v[3] = {0, 0, 0};
+        ok = clear || parse_ints(value, v, 3);
+        memcpy(p.rows, v, sizeof v);
+    } else if (!strcmp(key, "lmhead_decode")) {
+        int v[2] = {0, 0};
+        ok = clear || parse_ints(value, v, 2);
+        memcpy(p.decode, v, sizeof v);
+    } else if (!strcmp(key, "lmhead_kouter")) {
+        int v[4] = {0, 0, 0, 0};
+        if (clear) p.kouter = 0;
+        else if (!strcmp(value, "0")) p.kouter = -1;
+        else if ((ok = parse_ints(value, v, 4))) p.kouter = 1;
+        memcpy(p.kouter_shape, v, sizeof v);
+    } else if (!strcmp(key, "lmhead_gemm")) {
+        int v = 0;
+        ok = clear || !strcmp(value, "0") || parse_ints(value, &v, 1);
+        p.gemm = v;
+    } else if (!strcmp(key, "draft_tail")) {
+        ok = clear || !strcmp(value, "split");
+        p.draft_tail_split = clear ? 0 : 1;
+    } else if (!strcmp(key, "device_cus")) {
+        int v = 0;
+        ok = clear || parse_ints(value, &v, 1);
+        p.device_cus = v;
+    } else {
+        return fail(MTPD_ERR_SHAPE, "unknown plan-override key \"%s\"", key);
+    }
+    if (!ok) return fail(MTPD_ERR_SHAPE, "plan override %s: value \"%s\" does not parse", key, value);
+    g_plan = p;
+    return MTPD_OK;
+}
 
 const char* mtpd_status_name(mtpd_status s) {
     switch (s) {
@@ -132,7 +212,7 @@ const char* mtpd_last_error(void) { return g_err; }
 
 void mtpd_clear_error(void) { g_err[0] = 0; }
 
-int mtpd_abi_version(void) { return 4; }
+int mtpd_abi_version(void) { return 5; }
 
 const char* mtpd_lmhead_plan(int64_t n_rows, int64_t V, int64_t H) {
     thread_local char buf[160];

@@ -36,7 +36,8 @@ def test_exports_every_declared_symbol(L):
     assert {"mtpd_norm_quant", "mtpd_fp8_lmhead_argmax", "mtpd_draft_tail", "mtpd_workspace_bytes",
             "mtpd_status_name", "mtpd_last_error", "mtpd_clear_error", "mtpd_abi_version",
             "mtpd_lmhead_plan", "mtpd_draft_tail_plan", "mtpd_allreduce_norm_quant",
-            "mtpd_argmax_combine", "mtpd_fp8_lmhead_topk", "mtpd_topk_workspace_bytes"} <= set(names)
+            "mtpd_argmax_combine", "mtpd_fp8_lmhead_topk", "mtpd_topk_workspace_bytes",
+            "mtpd_set_plan_override"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -46,7 +47,7 @@ def test_status_names_and_version(L):
         "MTPD_OK", "MTPD_ERR_NULL", "MTPD_ERR_SHAPE", "MTPD_ERR_ALIGN", "MTPD_ERR_ALIAS",
         "MTPD_ERR_WORKSPACE", "MTPD_ERR_HIP"]
     assert L.mtpd_status_name(99).decode() == "MTPD_UNKNOWN"
-    assert L.mtpd_abi_version() == 4
+    assert L.mtpd_abi_version() == 5
 
 
 def test_workspace_bytes(L):
@@ -233,3 +234,33 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros((4, 256), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         m.norm_quant(x, x, torch.ones(256), 1e-6)
+
+
+def test_plan_override_parsing(L):
+    """The override setter rejects unknown keys and malformed values (changing
+    nothing), and the plan strings follow what it pins (host-only)."""
+    L.mtpd_set_plan_override(None, None)
+    auto = L.mtpd_lmhead_plan(24, 2048, 1536).decode()
+    for key, bad in [(b"nonsense", b"1"), (b"lmhead_kernel", b"fast"), (b"lmhead_tile", b"2,2"),
+                     (b"lmhead_tile", b"2,x,4"), (b"lmhead_stream", b"0,4"), (b"lmhead_kouter", b"1,2,3"),
+                     (b"draft_tail", b"fused"), (b"device_cus", b"-3"), (b"lmhead_rows", b"1,2,3,4")]:
+        L.mtpd_clear_error()
+        assert L.mtpd_set_plan_override(key, bad) == SHAPE, (key, bad)
+        assert L.mtpd_last_error().decode().startswith("MTPD_ERR_SHAPE")
+        assert L.mtpd_lmhead_plan(24, 2048, 1536).decode() == auto
+    try:
+        assert L.mtpd_set_plan_override(b"lmhead_kernel", b"generic") == OK
+        assert L.mtpd_set_plan_override(b"lmhead_tile", b"2,4,4") == OK
+        assert L.mtpd_lmhead_plan(24, 2048, 1536).decode().startswith("lmhead_argmax_kernel<2,2,4,4>")
+        assert L.mtpd_set_plan_override(b"lmhead_tile", None) == OK      # one key cleared
+        assert L.mtpd_lmhead_plan(24, 2048, 1536).decode().startswith("lmhead_argmax_kernel<")
+        assert L.mtpd_set_plan_override(b"draft_tail", b"split") == OK
+        assert L.mtpd_draft_tail_plan(1, 2048, 1024).decode().startswith("norm_quant_kernel")
+    finally:
+        assert L.mtpd_set_plan_override(None, None) == OK
+    assert L.mtpd_lmhead_plan(24, 2048, 1536).decode() == auto
+    assert L.mtpd_draft_tail_plan(1, 2048, 1024).decode().startswith("draft_tail1_kernel")
+    with m.plan_override(device_cus=8, lmhead_kouter="0"):
+        assert not L.mtpd_lmhead_plan(64, 4096, 1024).decode().startswith("lmhead_kouter")
+    with pytest.raises(KeyError):
+        m.plan_override(bogus=1)

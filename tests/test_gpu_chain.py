@@ -48,7 +48,7 @@ def test_chained_positions_stagewise_and_graph(name, K, workloads):
     w = d["workload"]
     say(f"chain {name}: K={K} M={w.M} H={w.H} V={w.V}")
     h, r, g, wc, ws = to_dev(d)
-    wsp = mtpd.Workspace(DEV)
+    wsp = mtpd.Workspace(DEV, any_stream=True)   # eager calls and a graph captured on a side stream
     wsp.get(w.M)
     outs = [_bufs(w.M, w.H) for _ in range(K)]
     _chain(h, r, g, d["eps"], wc, ws, outs, wsp)
