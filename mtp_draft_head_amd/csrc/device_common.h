@@ -98,6 +98,20 @@ __device__ __forceinline__ float row16_max(float v) {
     return fmaxf(v, dpp_f32<0x140>(v));
 }
 
+// Unsigned minimum over each 16-lane row, in every lane of the row.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    int r = __builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    asm volatile("" : "+v"(r));
+    return (uint32_t)r;
+}
+__device__ __forceinline__ uint32_t row16_min_u32(uint32_t v) {
+    v = min(v, dpp_u32<0xB1>(v));
+    v = min(v, dpp_u32<0x4E>(v));
+    v = min(v, dpp_u32<0x141>(v));
+    return min(v, dpp_u32<0x140>(v));
+}
+
 // u64 maximum over each 16-lane row, in every lane of the row.
 template <int CTRL>
 __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {

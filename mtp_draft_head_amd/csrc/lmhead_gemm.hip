@@ -298,17 +298,19 @@ __global__ __launch_bounds__(512) void lmhead_gemm_kernel(
 //    bytes], eight consecutive lanes per row's 128 bytes (a whole cache line
 //    per eight lanes: measured 12.4 against 10.7 TB/s of L2 -> LDS for four
 //    lanes per 64-byte half, copies alone, every CU busy), chunk c of row r
-//    at position c ^ ((r >> 1) & 7).
+//    at position c ^ ((r >> 1) & 7).  Global loads with a wave-uniform base
+//    and 32-bit lane offsets (buffer loads measured 5% slower).
 //  - MFMA lane l supplies row l % 16 and, for its 32 K bytes, 16-byte chunks
 //    l / 16 and l / 16 + 4 of that row (A and B permute K the same way, so
 //    the dot product is unchanged): each of the two fragment reads then
 //    touches 16 rows at one chunk each, and the swizzle spreads any 16
 //    consecutive lanes over all 64 banks.
-//  - Block scales: the activation scales of block kb + 1 travel with the
-//    codes of block kb; during block kb every thread forms one entry
-//    sa[row] * sw[block] of block kb + 1's scale table (2 weight-scale
-//    blocks x BM rows), so the promotion reads its factors instead of
-//    multiplying them per wave.
+//  - Block scales: the activation scales arrive eight K blocks at a time
+//    (32 bytes per row, two lanes per row: one request per eight rows'
+//    lines instead of one per row per block, which cost 15% of the copy
+//    rate); during block kb every thread forms one entry sa[row] * sw[block]
+//    of block kb + 1's factor table (2 weight-scale blocks x BM rows), so
+//    the promotion reads its factors instead of multiplying them per wave.
 //  - Per K block a wave issues its first row group's activation fragment and
 //    factors and its four weight fragments, then starts each of the first
 //    group's MFMAs as soon as that MFMA's own operands have arrived (reads
@@ -326,15 +328,16 @@ struct G2 {
     static constexpr int BM = 32 * MT;                // activation rows per tile
     static constexpr int A_BYTES = BM * 128;          // activation tile, [row][128 bytes]
     static constexpr int W_BYTES = 256 * 128;         // weight tile
-    static constexpr int SA_FLOATS = (BM + 63) / 64 * 64;
     // LDS, operand-major so that one base register per fragment half reaches
     // both stages through the 16-bit immediate offset: [A stage 0][A stage 1]
-    // [W stage 0][W stage 1][scales stage 0][scales stage 1]
+    // [W stage 0][W stage 1][scale chunk 0][scale chunk 1]
     static constexpr int W_OFF = 2 * A_BYTES;
-    static constexpr int SA_OFF = W_OFF + 2 * W_BYTES;
-    static constexpr int SMEM = SA_OFF + 2 * SA_FLOATS * 4;
+    static constexpr int SC_OFF = W_OFF + 2 * W_BYTES;
+    static constexpr int SC_BLOCKS = 8;               // K blocks per scale chunk
+    static constexpr int SC_BYTES = BM * SC_BLOCKS * 4;   // [row][8] fp32
+    static constexpr int SMEM = SC_OFF + 2 * SC_BYTES;
     static constexpr int A_COPIES = BM / 8;           // copies of 8 rows x 128 bytes
-    static constexpr int SCOPY = SA_FLOATS / 64;      // scale copies of 64 rows
+    static constexpr int SCOPY = BM / 32;             // scale-chunk copies of 32 rows x 32 bytes
     static constexpr int SW_MAX = 64;                 // K blocks of the weight-scale table (H <= 8192)
     static_assert(A_BYTES + 7 * 2048 < 65536 && W_BYTES + 6 * 2048 < 65536, "immediate offsets");
 };
@@ -414,20 +417,16 @@ __device__ __forceinline__ void dma4(const void* src, void* lds) {
     __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds, 4, 0, 0);
 }
 
-// The same copies through a raw buffer resource: a 32-bit per-lane byte
-// offset plus a wave-uniform one, no 64-bit address arithmetic per copy
-// (the global form's per-copy address pairs, hoisted out of the K loop, ran
-// the register file out).  Third descriptor word: 32-bit data format, the
-// raw-buffer setting of this architecture family.
+// The same copy through a raw buffer resource of a given size: lanes whose
+// byte offset lies past the end read zeros instead of faulting.  Third
+// descriptor word: 32-bit data format, the raw-buffer setting of this
+// architecture family.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 __device__ __forceinline__ void bdma16(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void bdma4(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
 }
 
 // hides a value from constant folding (the zero accumulators of the first block)
@@ -440,7 +439,7 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
     const uint8_t* __restrict__ a_codes, const float* __restrict__ a_scales,
     const int32_t* __restrict__ row_index, int n_rows,
     const uint8_t* __restrict__ w_codes, const float* __restrict__ w_scales, int H,
-    int n_row_tiles, int n_col_tiles, int group_rows,
+    int n_row_tiles, int n_col_tiles, int group_rows, uint32_t scale_bytes,
     float* __restrict__ out_max, int32_t* __restrict__ out_idx, ArgmaxWs ws)
 {
     using C = G2<MT>;
@@ -475,10 +474,11 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
     // Copy j of an operand moves rows 8j .. 8j + 7: lane i lands at position
     // i & 7 of row 8j + (i >> 3), so it reads the chunk stored there.
     // Activation copies j = wave, wave + 8, ... (rows past n_rows repeat its
-    // last row); weight copies 4 * wave .. 4 * wave + 3; scale copy `wave` on
-    // the first SCOPY waves (64 rows; rows past the tile repeat its last row).
-    // Offsets are 32-bit from wave-uniform bases (the host keeps the
-    // activation and its scales under 2 GiB for this kernel).
+    // last row); weight copies 4 * wave .. 4 * wave + 3; scale-chunk copy
+    // `wave` on the first SCOPY waves (rows 32w .. 32w + 31, lanes 2q, 2q + 1
+    // the two halves of row q's 32 bytes; rows past n_rows repeat its last
+    // row).  Offsets are 32-bit from wave-uniform bases (the host keeps the
+    // activation under 2 GiB for this kernel).
     const int crow = lane >> 3;
     constexpr int AC = (C::A_COPIES + 7) / 8;
     uint32_t aoff[AC], woff[4];
@@ -495,25 +495,30 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
         const int r = (4 * wave + i) * 8 + crow;
         woff[i] = (uint32_t)r * (uint32_t)H + (uint32_t)chunk_pos(r, lane & 7) * 16u;
     }
-    const rsrc_t a_rs = make_rsrc(a_codes);
-    const rsrc_t w_rs = make_rsrc(w_codes + (size_t)n0 * (size_t)H);
-    const rsrc_t s_rs = make_rsrc(a_scales);
-    const int sa_row = min(m0 + min(wave * 64 + lane, BM - 1), n_rows - 1);
-    const uint32_t saoff = (uint32_t)(row_index ? row_index[sa_row] : sa_row) * (uint32_t)KB * 4u;
+    const uint8_t* wbase = w_codes + (size_t)n0 * (size_t)H;
+    // the scale chunks through a buffer resource of the scales' exact size: a
+    // last chunk that runs past a row's K blocks reads the next row's scales
+    // (unused), or zeros past the end of the array, never unmapped memory
+    const rsrc_t s_rs = make_rsrc(a_scales, scale_bytes);
+    const int sc_row = min(m0 + min(wave * 32 + (lane >> 1), BM - 1), n_rows - 1);
+    const uint32_t scoff = (uint32_t)(row_index ? row_index[sc_row] : sc_row) * (uint32_t)KB * 4u + (uint32_t)(lane & 1) * 16u;
 
-    // codes of block kb and activation scales of block skb into stage s
-    auto copy_in = [&](int s, int kb, int skb) {
-        const uint32_t kofs = (uint32_t)kb * kBlock;
+    // codes of block kb into stage s
+    auto copy_in = [&](int s, int kb) {
+        const uint8_t* ab = a_codes + (size_t)kb * kBlock;
+        const uint8_t* wb = wbase + (size_t)kb * kBlock;
 #pragma unroll
         for (int i = 0; i < AC; ++i) {
             const int j = wave + 8 * i;
-            if (j < C::A_COPIES) bdma16(a_rs, aoff[i], kofs, smem + s * C::A_BYTES + j * 1024);
+            if (j < C::A_COPIES) dma16(ab + aoff[i], smem + s * C::A_BYTES + j * 1024);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            bdma16(w_rs, woff[i], kofs, smem + C::W_OFF + s * C::W_BYTES + (4 * wave + i) * 1024);
+        for (int i = 0; i < 4; ++i) dma16(wb + woff[i], smem + C::W_OFF + s * C::W_BYTES + (4 * wave + i) * 1024);
+    };
+    // activation scales of K blocks 8c .. 8c + 7 into chunk slot c % 2
+    auto copy_scales = [&](int c) {
         if (wave < C::SCOPY)
-            bdma4(s_rs, saoff, (uint32_t)skb * 4u, smem + C::SA_OFF + s * C::SA_FLOATS * 4 + wave * 256);
+            bdma16(s_rs, scoff + (uint32_t)c * 32u, 0u, smem + C::SC_OFF + (c & 1) * C::SC_BYTES + wave * 1024);
     };
 
     // ---- fragment addresses (bytes in LDS), one set per stage ----
@@ -635,59 +640,65 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
         promote(MT - 1, 3, ring[1], fv[(MT - 1) & 1]);
     };
 
-    // promotion factors of block kb from the activation scales in a stage
+    // promotion factors of block kb from its scale chunk
     // (thread t: weight-scale block t / BM, row t % BM)
-    auto factors = [&](int slot, int s, int kb) {
+    auto factors = [&](int slot, int kb) {
+        const float* chunk = reinterpret_cast<const float*>(smem + C::SC_OFF + ((kb >> 3) & 1) * C::SC_BYTES);
         for (int e = t; e < 2 * BM; e += 512) {
             const int cb = e / BM, r = e - cb * BM;
-            const float sa = reinterpret_cast<const float*>(smem + C::SA_OFF + s * C::SA_FLOATS * 4)[r];
-            ftab[slot][cb][r] = sa * swtab[cb][kb];
+            ftab[slot][cb][r] = chunk[r * C::SC_BLOCKS + (kb & 7)] * swtab[cb][kb];
         }
     };
 
     // ---- pipeline ----
-    // Prologue: the weight-scale table, block 0's activation scales (into
-    // stage 1's scale slot, idle until block 1's copy), stage 0 = codes of
-    // block 0 with the scales of block 1; then block 0's factors.
-    // Block kb computes from stage kb % 2 and factor slot kb % 2, while the
-    // copy of block kb + 1 (with the scales of block kb + 2) fills the other
-    // stage and every thread forms one factor of block kb + 1 from the scales
-    // stage kb holds; the barrier ending the block publishes both.
+    // Prologue: the weight-scale table, scale chunks 0 and 1, stage 0 = codes
+    // of block 0; then block 0's factors.  Block kb computes from stage kb % 2
+    // and factor slot kb % 2, while the copy of block kb + 1 fills the other
+    // stage and every thread forms one factor of block kb + 1; the barrier
+    // ending the block publishes both.  Chunk c + 1 is copied at the start of
+    // block 8c (c >= 1): chunk c - 1, in that slot, was last read during block
+    // 8c - 2.
     if (wave < 2)
         dma4(w_scales + (size_t)((n0 >> 7) + wave) * KB + min(lane, KB - 1), &swtab[wave][0]);
-    if (wave < C::SCOPY) bdma4(s_rs, saoff, 0u, smem + C::SA_OFF + C::SA_FLOATS * 4 + wave * 256);
-    copy_in(0, 0, min(1, KB - 1));
+    copy_scales(0);
+    if (KB > C::SC_BLOCKS) copy_scales(1);
+    copy_in(0, 0);
     drain_barrier();
-    factors(0, 1, 0);
+    factors(0, 0);
     drain_barrier();
     for (int kb = 0; kb < KB; kb += 2) {
-        // stage 0
-        if (kb + 1 < KB) copy_in(1, kb + 1, min(kb + 2, KB - 1));
+        // stage 0 (kb is even: chunk boundaries fall here)
+        if (kb + 1 < KB) copy_in(1, kb + 1);
+        if (kb > 0 && (kb & 7) == 0 && kb + C::SC_BLOCKS < KB) copy_scales((kb >> 3) + 1);
         compute(0);
-        if (kb + 1 < KB) factors(1, 0, kb + 1);
+        if (kb + 1 < KB) factors(1, kb + 1);
         drain_barrier();
         if (kb + 1 >= KB) break;
         // stage 1
-        if (kb + 2 < KB) copy_in(0, kb + 2, min(kb + 3, KB - 1));
+        if (kb + 2 < KB) copy_in(0, kb + 2);
         compute(1);
-        if (kb + 2 < KB) factors(0, 1, kb + 2);
+        if (kb + 2 < KB) factors(0, kb + 2);
         drain_barrier();
     }
 
     // ---- epilogue: per-row best over the wave's 64 columns, then over the
-    // four column waves (table in the now idle stage memory) ----
+    // four column waves (table in the now idle stage memory).  A row's best
+    // is its largest fp32 value and the lowest column holding it (fp32
+    // compares treat -0 and +0 as equal, as the key does): the 32-bit
+    // reductions cost a third of reducing 64-bit keys. ----
     unsigned long long* red = reinterpret_cast<unsigned long long*>(smem);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            uint64_t best = 0;
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-                best = u64_max(best, argmax_key(acc[mt][nt][i],
-                                                (uint32_t)(n0 + wn * 64 + nt * 16 + (lane & 15))));
-            best = row16_max_u64(best);
-            if ((lane & 15) == 0) red[wn * BM + wm * MT * 16 + mt * 16 + 4 * (lane >> 4) + i] = best;
+            const float v0 = acc[mt][0][i], v1 = acc[mt][1][i], v2 = acc[mt][2][i], v3 = acc[mt][3][i];
+            const float rm = row16_max(fmaxf(fmaxf(v0, v1), fmaxf(v2, v3)));
+            // this lane's columns are lane % 16 + 16 nt, increasing with nt
+            const uint32_t c = v0 == rm ? 0u : (v1 == rm ? 16u : (v2 == rm ? 32u : (v3 == rm ? 48u : 0x10000u)));
+            const uint32_t col = row16_min_u32(c + (uint32_t)(lane & 15));
+            if ((lane & 15) == 0)
+                red[wn * BM + wm * MT * 16 + mt * 16 + 4 * (lane >> 4) + i] =
+                    argmax_key(rm, (uint32_t)(n0 + wn * 64) + col);
         }
     }
     __syncthreads();
@@ -720,7 +731,8 @@ hipError_t launch_gemm2(const LmheadArgs& a, int group_rows, hipStream_t stream)
     const int gr = (int)std::max<int64_t>(1, std::min<int64_t>(group_rows, row_tiles));
     hipLaunchKernelGGL((lmhead_gemm2_kernel<MT>), dim3((unsigned)(row_tiles * col_tiles)), dim3(512), 0, stream,
                        a.a_codes, a.a_scales, a.row_index, (int)a.n_rows, a.w_codes, a.w_scales, (int)a.H,
-                       (int)row_tiles, (int)col_tiles, gr, a.out_max, a.out_idx, argmax_ws(a.workspace, a.n_rows));
+                       (int)row_tiles, (int)col_tiles, gr, (uint32_t)(a.a_rows * (a.H / 128) * 4), a.out_max,
+                       a.out_idx, argmax_ws(a.workspace, a.n_rows));
     return hipGetLastError();
 }
 
