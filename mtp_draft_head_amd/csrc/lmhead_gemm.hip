@@ -333,13 +333,14 @@ struct G2 {
     // [W stage 0][W stage 1][scale chunk 0][scale chunk 1]
     static constexpr int W_OFF = 2 * A_BYTES;
     static constexpr int SC_OFF = W_OFF + 2 * W_BYTES;
-    static constexpr int SC_BLOCKS = 8;               // K blocks per scale chunk
-    static constexpr int SC_BYTES = BM * SC_BLOCKS * 4;   // [row][8] fp32
+    static constexpr int SC_BLOCKS = BM > 256 ? 4 : 8;   // K blocks per scale chunk (LDS budget)
+    static constexpr int SC_BYTES = BM * SC_BLOCKS * 4;   // [row][SC_BLOCKS] fp32
+    static constexpr int SC_LANES = SC_BLOCKS / 4;        // lanes per row of a chunk copy (16 bytes each)
     static constexpr int SMEM = SC_OFF + 2 * SC_BYTES;
     static constexpr int A_COPIES = BM / 8;           // copies of 8 rows x 128 bytes
-    static constexpr int SCOPY = BM / 32;             // scale-chunk copies of 32 rows x 32 bytes
+    static constexpr int SCOPY = BM * SC_LANES / 64;  // scale-chunk copies (64 lanes x 16 bytes)
     static constexpr int SW_MAX = 64;                 // K blocks of the weight-scale table (H <= 8192)
-    static_assert(A_BYTES + 7 * 2048 < 65536 && W_BYTES + 6 * 2048 < 65536, "immediate offsets");
+    static_assert(MT <= 12, "row groups per wave (immediate-offset cases)");
 };
 
 // position of 16-byte chunk c of row r inside the row's 128 bytes
@@ -353,18 +354,21 @@ __device__ __forceinline__ u32x4_t lds_read16_off(uint32_t addr) {
 }
 
 // lds_read16_off<s * SBYTES + k * STEP>(addr) for a stage s (0, 1) and a k
-// (0..7) known after unrolling
+// (0..11) known after unrolling
 template <int SBYTES, int STEP>
 __device__ __forceinline__ u32x4_t lds_read16_sk(uint32_t addr, int s, int k) {
+    static_assert(SBYTES + 11 * STEP < 65536, "immediate offset range");
 #define MTPD_CASE(S, K) \
-    case S * 8 + K: return lds_read16_off<S * SBYTES + K * STEP>(addr);
-    switch (s * 8 + k) {
-        MTPD_CASE(0, 0) MTPD_CASE(0, 1) MTPD_CASE(0, 2) MTPD_CASE(0, 3)
-        MTPD_CASE(0, 4) MTPD_CASE(0, 5) MTPD_CASE(0, 6) MTPD_CASE(0, 7)
-        MTPD_CASE(1, 0) MTPD_CASE(1, 1) MTPD_CASE(1, 2) MTPD_CASE(1, 3)
-        MTPD_CASE(1, 4) MTPD_CASE(1, 5) MTPD_CASE(1, 6)
-        default: return lds_read16_off<SBYTES + 7 * STEP>(addr);
+    case S * 16 + K: return lds_read16_off<S * SBYTES + K * STEP>(addr);
+#define MTPD_CASES(S)                                                                                     \
+    MTPD_CASE(S, 0) MTPD_CASE(S, 1) MTPD_CASE(S, 2) MTPD_CASE(S, 3) MTPD_CASE(S, 4) MTPD_CASE(S, 5)      \
+    MTPD_CASE(S, 6) MTPD_CASE(S, 7) MTPD_CASE(S, 8) MTPD_CASE(S, 9) MTPD_CASE(S, 10) MTPD_CASE(S, 11)
+    switch (s * 16 + k) {
+        MTPD_CASES(0)
+        MTPD_CASES(1)
+        default: __builtin_unreachable();
     }
+#undef MTPD_CASES
 #undef MTPD_CASE
 }
 
@@ -500,8 +504,9 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
     // last chunk that runs past a row's K blocks reads the next row's scales
     // (unused), or zeros past the end of the array, never unmapped memory
     const rsrc_t s_rs = make_rsrc(a_scales, scale_bytes);
-    const int sc_row = min(m0 + min(wave * 32 + (lane >> 1), BM - 1), n_rows - 1);
-    const uint32_t scoff = (uint32_t)(row_index ? row_index[sc_row] : sc_row) * (uint32_t)KB * 4u + (uint32_t)(lane & 1) * 16u;
+    const int sc_row = min(m0 + min((wave * 64 + lane) / C::SC_LANES, BM - 1), n_rows - 1);
+    const uint32_t scoff = (uint32_t)(row_index ? row_index[sc_row] : sc_row) * (uint32_t)KB * 4u +
+                           (uint32_t)(lane % C::SC_LANES) * 16u;
 
     // codes of block kb into stage s
     auto copy_in = [&](int s, int kb) {
@@ -515,10 +520,11 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16(wb + woff[i], smem + C::W_OFF + s * C::W_BYTES + (4 * wave + i) * 1024);
     };
-    // activation scales of K blocks 8c .. 8c + 7 into chunk slot c % 2
+    // activation scales of K blocks c * SC_BLOCKS .. + SC_BLOCKS - 1 into chunk slot c % 2
     auto copy_scales = [&](int c) {
         if (wave < C::SCOPY)
-            bdma16(s_rs, scoff + (uint32_t)c * 32u, 0u, smem + C::SC_OFF + (c & 1) * C::SC_BYTES + wave * 1024);
+            bdma16(s_rs, scoff + (uint32_t)(c * C::SC_BLOCKS) * 4u, 0u,
+                   smem + C::SC_OFF + (c & 1) * C::SC_BYTES + wave * 1024);
     };
 
     // ---- fragment addresses (bytes in LDS), one set per stage ----
@@ -643,10 +649,11 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
     // promotion factors of block kb from its scale chunk
     // (thread t: weight-scale block t / BM, row t % BM)
     auto factors = [&](int slot, int kb) {
-        const float* chunk = reinterpret_cast<const float*>(smem + C::SC_OFF + ((kb >> 3) & 1) * C::SC_BYTES);
+        const float* chunk =
+            reinterpret_cast<const float*>(smem + C::SC_OFF + ((kb / C::SC_BLOCKS) & 1) * C::SC_BYTES);
         for (int e = t; e < 2 * BM; e += 512) {
             const int cb = e / BM, r = e - cb * BM;
-            ftab[slot][cb][r] = chunk[r * C::SC_BLOCKS + (kb & 7)] * swtab[cb][kb];
+            ftab[slot][cb][r] = chunk[r * C::SC_BLOCKS + kb % C::SC_BLOCKS] * swtab[cb][kb];
         }
     };
 
@@ -669,7 +676,7 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
     for (int kb = 0; kb < KB; kb += 2) {
         // stage 0 (kb is even: chunk boundaries fall here)
         if (kb + 1 < KB) copy_in(1, kb + 1);
-        if (kb > 0 && (kb & 7) == 0 && kb + C::SC_BLOCKS < KB) copy_scales((kb >> 3) + 1);
+        if (kb > 0 && kb % C::SC_BLOCKS == 0 && kb + C::SC_BLOCKS < KB) copy_scales(kb / C::SC_BLOCKS + 1);
         compute(0);
         if (kb + 1 < KB) factors(1, kb + 1);
         drain_barrier();
@@ -738,23 +745,28 @@ hipError_t launch_gemm2(const LmheadArgs& a, int group_rows, hipStream_t stream)
 
 int gemm_variant(int64_t n_rows, int64_t H, int64_t a_rows) {
     const int o = plan_override().gemm;
-    if (o >= 1 && o <= 6) return o;
+    if (o >= 1 && o <= 8) return o;
     // the pipelined kernel takes H <= 8192 (its weight-scale table) and an
     // activation under 2 GiB (32-bit buffer offsets)
     if (H > 128 * G2<8>::SW_MAX || a_rows * H >= ((int64_t)1 << 31)) return 1;
     // tile height: fewest copied bytes, row tiles x (tile rows + 256 weight
-    // rows) per K block (320 rows: two 160-row tiles, not two 256-row tiles
-    // of which 192 rows are padding)
-    const int64_t c8 = (n_rows + 255) / 256 * (256 + 256), c5 = (n_rows + 159) / 160 * (160 + 256);
+    // rows) per K block; the 320-row tile (its LDS full, scale chunks of four
+    // blocks, every register in use) measured about 10% slower per byte, so
+    // it is charged 10% more.  320 rows: one 320-row tile (each weight tile
+    // copied once), not two 256-row tiles of which 192 rows are padding.
+    const int64_t c8 = (n_rows + 255) / 256 * (256 + 256) * 10, c5 = (n_rows + 159) / 160 * (160 + 256) * 10;
+    const int64_t c10 = (n_rows + 319) / 320 * (320 + 256) * 11;
+    if (c10 < c8 && c10 < c5) return 8;
     return c5 < c8 ? 6 : 3;
 }
 
 void describe_gemm(int64_t n_rows, int64_t V, int64_t H, int64_t a_rows, char* buf, size_t len) {
     const int v = gemm_variant(n_rows, H, a_rows);
-    const int bm = v == 1 ? 256 : (v <= 4 ? 256 : 160);
+    const int bm = v == 1 ? 256 : (v <= 4 ? 256 : (v <= 6 ? 160 : 320));
     const long long tiles = (long long)((n_rows + bm - 1) / bm * (V / 256));
     if (v == 1) snprintf(buf, len, "lmhead_gemm_kernel grid=%lldx512", tiles);
-    else snprintf(buf, len, "lmhead_gemm2_kernel<%d> grid=%lldx512 group=%d", bm / 32, tiles, v == 2 || v == 5 ? 4 : (v == 4 ? 16 : 8));
+    else snprintf(buf, len, "lmhead_gemm2_kernel<%d> grid=%lldx512 group=%d", bm / 32, tiles,
+                  v == 2 || v == 5 || v == 7 ? 4 : (v == 4 ? 16 : 8));
 }
 
 hipError_t launch_lmhead_gemm(const LmheadArgs& a, hipStream_t stream) {
@@ -765,6 +777,8 @@ hipError_t launch_lmhead_gemm(const LmheadArgs& a, hipStream_t stream) {
         case 4: return launch_gemm2<8>(a, 16, stream);
         case 5: return launch_gemm2<5>(a, 4, stream);
         case 6: return launch_gemm2<5>(a, 8, stream);
+        case 7: return launch_gemm2<10>(a, 4, stream);
+        case 8: return launch_gemm2<10>(a, 8, stream);
         default: break;
     }
     const int64_t row_tiles = (a.n_rows + kBM - 1) / kBM;

@@ -394,9 +394,11 @@ def test_block_scales_across_the_exponent_range():
 
 # compute-regime kernel variants (plan override lmhead_gemm): 1 the
 # single-wait kernel, 2-4 pipelined 256-row tiles (row-tile groups 4, 8, 16),
-# 5-6 pipelined 160-row tiles; ragged M and odd K block counts
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6])
-@pytest.mark.parametrize("M,H,V", [(300, 1152, 1536), (65, 128, 512), (517, 2176, 2304), (160, 640, 768)])
+# 5-6 pipelined 160-row tiles, 7-8 pipelined 320-row tiles; ragged M and odd
+# K block counts (including fewer blocks than a scale chunk)
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("M,H,V", [(300, 1152, 1536), (65, 128, 512), (517, 2176, 2304), (160, 640, 768),
+                                   (700, 1664, 1024)])
 def test_gemm_variants(variant, M, H, V):
     """Every compute-regime variant meets the oracle on every row and picks the
     same indices as the generic kernel outside near ties (all variants sum the
@@ -412,7 +414,7 @@ def test_gemm_variants(variant, M, H, V):
     assert torch.equal(i, i1) and torch.equal(m, m1)
 
 
-@pytest.mark.parametrize("variant", [2, 5])
+@pytest.mark.parametrize("variant", [2, 5, 7])
 def test_gemm_variants_row_index(variant):
     """Gathered rows (repeats included) through the pipelined kernels give the
     ungathered call's pairs."""
