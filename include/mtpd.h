@@ -151,6 +151,25 @@ mtpd_status mtpd_draft_tail(const uint16_t *hidden, const uint16_t *residual,
                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * mtpd_draft_tail for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same arguments without the workspace, the
+ * same kernels and bit-identical results.  The argmax keys and arrival
+ * counters live in a device array inside the library, 528640 bytes per GPU
+ * (held until the process ends), which covers M <= 65536; a larger M returns
+ * MTPD_ERR_WORKSPACE and launches nothing.  The first call on a device
+ * clears that array with a fill kernel on `stream`; every completed call
+ * leaves it clear again.  The array is shared by every call on the same GPU:
+ * calls that overlap in time on one GPU (two streams, two threads) race and
+ * give wrong results; serialize them.  Never calls hipMalloc or hipFree.
+ */
+mtpd_status mtpd_draft_tail_noalloc(const uint16_t *hidden, const uint16_t *residual,
+                                    const float *norm_weight, float eps, int64_t M, int64_t H,
+                                    const mtpd_fp8_weight *w, uint16_t *out_hidden,
+                                    const mtpd_qact *out_act, float *out_max, int32_t *out_idx,
+                                    void *stream);
+
+/*
  * mtpd_norm_quant with the MTP layer's trailing all-reduce folded in
  * ("Fuse the MTP trailing all-reduce; local-argmax draft tokens", Summary:
  * all-reduce and RMSNorm as one fused step; Accuracy: fp32 accumulation).

@@ -119,6 +119,9 @@ def lib():
         L.mtpd_draft_tail_plan.argtypes = [I64, I64, I64]
         L.mtpd_abi_version.restype = ctypes.c_int
         L.mtpd_abi_version.argtypes = []
+        L.mtpd_draft_tail_noalloc.restype = ctypes.c_int
+        L.mtpd_draft_tail_noalloc.argtypes = [P, P, P, F, I64, I64, ctypes.POINTER(FP8Weight), P,
+                                              ctypes.POINTER(QAct), P, P, P]
         L.mtpd_set_plan_override.restype = ctypes.c_int
         L.mtpd_set_plan_override.argtypes = [ctypes.c_char_p, ctypes.c_char_p]
         _lib = L

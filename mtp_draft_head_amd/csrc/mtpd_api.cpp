@@ -114,6 +114,25 @@ mtpd_status hip_status(hipError_t e, const char* what) {
 
 mtpd::PlanOverride g_plan{};
 
+// ---- scratch of the allocation-free entry point ----
+// The argmax keys and arrival counters of mtpd_draft_tail_noalloc live in one
+// file-scope device array (one copy per GPU, held until the process ends),
+// sized for 65536 rows: the largest workspace_bytes(n) for n <= 65536 is
+// 512 KiB of keys plus the counter lines.  Host code never uses the array's
+// name as an address: each device's address comes from hipGetSymbolAddress.
+constexpr int64_t kNoallocMaxRows = 65536;
+constexpr size_t kScratchBytes = 524288 + (size_t)(mtpd::kArriveGroups + 1) * 128 + 128;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {nullptr};
+bool g_scratch_zeroed[kMaxDevices] = {false};
+
+__global__ void zero_fill_kernel(uint4* __restrict__ p, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 // "a,b,c" -> n ints, all positive; false if it does not parse
 bool parse_ints(const char* v, int* out, int n) {
     int got = 0;
@@ -212,7 +231,7 @@ const char* mtpd_last_error(void) { return g_err; }
 
 void mtpd_clear_error(void) { g_err[0] = 0; }
 
-int mtpd_abi_version(void) { return 5; }
+int mtpd_abi_version(void) { return 6; }
 
 const char* mtpd_lmhead_plan(int64_t n_rows, int64_t V, int64_t H) {
     thread_local char buf[160];
@@ -297,7 +316,7 @@ mtpd_status mtpd_fp8_lmhead_argmax(const mtpd_qact* act, const int32_t* row_inde
     return hip_status(mtpd::launch_lmhead_argmax(a, (hipStream_t)stream), "lmhead_argmax launch");
 }
 
-mtpd_status mtpd_draft_tail(const uint16_t* hidden, const uint16_t* residual, const float* norm_weight, float eps,
+static mtpd_status draft_tail_impl(const uint16_t* hidden, const uint16_t* residual, const float* norm_weight, float eps,
                             int64_t M, int64_t H, const mtpd_fp8_weight* w, uint16_t* out_hidden,
                             const mtpd_qact* out_act, float* out_max, int32_t* out_idx, void* workspace,
                             size_t workspace_bytes, void* stream) {
@@ -335,6 +354,49 @@ mtpd_status mtpd_draft_tail(const uint16_t* hidden, const uint16_t* residual, co
     mtpd::LmheadArgs a{out_act->codes, out_act->scales, nullptr, M, M, w->codes, w->scales, w->V, H,
                        out_max, out_idx, workspace};
     return hip_status(mtpd::launch_lmhead_argmax(a, s), "lmhead_argmax launch");
+}
+
+mtpd_status mtpd_draft_tail(const uint16_t* hidden, const uint16_t* residual, const float* norm_weight, float eps,
+                            int64_t M, int64_t H, const mtpd_fp8_weight* w, uint16_t* out_hidden,
+                            const mtpd_qact* out_act, float* out_max, int32_t* out_idx, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    return draft_tail_impl(hidden, residual, norm_weight, eps, M, H, w, out_hidden, out_act, out_max, out_idx,
+                           workspace, workspace_bytes, stream);
+}
+
+mtpd_status mtpd_draft_tail_noalloc(const uint16_t* hidden, const uint16_t* residual, const float* norm_weight,
+                                    float eps, int64_t M, int64_t H, const mtpd_fp8_weight* w, uint16_t* out_hidden,
+                                    const mtpd_qact* out_act, float* out_max, int32_t* out_idx, void* stream) {
+    if (M > kNoallocMaxRows)
+        return fail(MTPD_ERR_WORKSPACE, "M=%lld exceeds the %lld rows the no-alloc scratch holds", (long long)M,
+                    (long long)kNoallocMaxRows);
+    if (M <= 0) {   // argument checks only; nothing is launched
+        return draft_tail_impl(hidden, residual, norm_weight, eps, M, H, w, out_hidden, out_act, out_max, out_idx,
+                               nullptr, 0, stream);
+    }
+    int dev = -1;
+    mtpd_status st = hip_status(hipGetDevice(&dev), "hipGetDevice");
+    if (st != MTPD_OK) return st;
+    if (dev < 0 || dev >= kMaxDevices) return fail(MTPD_ERR_HIP, "device %d out of range", dev);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        st = hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (st != MTPD_OK) return st;
+        g_scratch_ptr[dev] = ptr;
+    }
+    void* ptr = g_scratch_ptr[dev];
+    if (!g_scratch_zeroed[dev]) {
+        // the keys and counters must start at zero; every completed call
+        // leaves them zero again.  A fill kernel, not a memset, so that a
+        // first call inside a graph capture stays correct on every replay.
+        hipLaunchKernelGGL(zero_fill_kernel, dim3(256), dim3(256), 0, (hipStream_t)stream, (uint4*)ptr,
+                           kScratchBytes / 16);
+        st = hip_status(hipGetLastError(), "scratch zero-fill launch");
+        if (st != MTPD_OK) return st;
+        g_scratch_zeroed[dev] = true;
+    }
+    return draft_tail_impl(hidden, residual, norm_weight, eps, M, H, w, out_hidden, out_act, out_max, out_idx, ptr,
+                           kScratchBytes, stream);
 }
 
 mtpd_status mtpd_allreduce_norm_quant(const uint16_t* const* partials, int64_t n_partials, const uint16_t* residual,

@@ -47,7 +47,7 @@ def test_status_names_and_version(L):
         "MTPD_OK", "MTPD_ERR_NULL", "MTPD_ERR_SHAPE", "MTPD_ERR_ALIGN", "MTPD_ERR_ALIAS",
         "MTPD_ERR_WORKSPACE", "MTPD_ERR_HIP"]
     assert L.mtpd_status_name(99).decode() == "MTPD_UNKNOWN"
-    assert L.mtpd_abi_version() == 5
+    assert L.mtpd_abi_version() == 6
 
 
 def test_workspace_bytes(L):
@@ -264,3 +264,17 @@ def test_plan_override_parsing(L):
         assert not L.mtpd_lmhead_plan(64, 4096, 1024).decode().startswith("lmhead_kouter")
     with pytest.raises(KeyError):
         m.plan_override(bogus=1)
+
+
+def test_noalloc_rejects_too_many_rows(L):
+    """The allocation-free tail refuses M beyond its scratch before any HIP call;
+    its scratch covers the workspace of the largest M it accepts."""
+    assert L.mtpd_workspace_bytes(65536) <= 528640
+    qa = QAct(0x10000000, 0x20000000, 65537, 256)
+    w = FP8Weight(0x30000000, 0x40000000, 256, 256)
+    L.mtpd_clear_error()
+    st = L.mtpd_draft_tail_noalloc(0x50000000, 0x60000000, 0x70000000, 1e-6, 65537, 256, ctypes.byref(w),
+                                   0x80000000, ctypes.byref(qa), 0x90000000, 0xA0000000, None)
+    assert st == 5, st   # MTPD_ERR_WORKSPACE, before any HIP call
+    assert "65536" in L.mtpd_last_error().decode()
+    L.mtpd_clear_error()
