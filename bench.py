@@ -223,7 +223,8 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, copy_mib: int, 
     out["traffic_over_algorithmic"] = total / alg
     vflag = "" if variant == "tail" else f" --variant {variant}"
     tag = workload if variant == "tail" else f"{workload}_{variant}"
-    run = (f"python3 bench.py --no-cpu-baseline --workload {workload}{vflag} --steps 20 --warmup 5 "
+    run = (f"python3 bench.py --no-cpu-baseline --no-peaks --no-companions --workload {workload}{vflag} "
+           f"--steps 20 --warmup 5 "
            f"--copy-calibration-mib {copy_mib}")
     out["commands"] = [
         f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcf_{tag} -o run -- {run}",
@@ -232,6 +233,61 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, copy_mib: int, 
         f"gpurun_out/pmcf_{tag}/run_counter_collection.csv gpurun_out/pmcw_{tag}/run_counter_collection.csv",
     ]
     dst = traffic_path(kname, workload, variant)
+    with open(dst, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
+
+
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F6F4")
+N_XCC, N_SIMD = 8, 1024   # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def summarize_mfma(workload: str, csv_path: str, bench_log: str) -> int:
+    """Matrix-core utilisation of the step's dominant kernel from one
+    rocprofv3 --pmc run of MFMA_COUNTERS: busy = SQ_VALU_MFMA_BUSY_CYCLES
+    (summed over every SIMD) / (GRBM_GUI_ACTIVE per XCC x 1024 SIMDs);
+    flops = (MOPS_F8 + MOPS_F6F4) x 512 (one MOP is 512 flops); the clock is
+    GRBM_GUI_ACTIVE per XCC over the kernel's time in the same run's bench
+    line.  Writes profiles/<kernel>_<workload>_mfma.json (and prints it)."""
+    from mtp_draft_head_amd import inputs
+
+    w = inputs.get(workload)
+    kname, _, _, plan, flops_alg = roofline_kernel("tail", w.M, w.H, w.V)
+    per = {}
+    for k, c, v, disp in _read_counters(csv_path):
+        if kname in k and c in MFMA_COUNTERS:
+            per.setdefault(disp, {}).setdefault(c, 0.0)
+            per[disp][c] += v
+    runs = [d for d in per.values() if all(c in d for c in MFMA_COUNTERS)]
+    if not runs:
+        print(f"no {kname} dispatch with all of {MFMA_COUNTERS} in {csv_path}", file=sys.stderr)
+        return 1
+    line = None
+    with open(bench_log) as f:
+        for ln in f:
+            if ln.startswith("{"):
+                line = json.loads(ln)
+    us = line["lmhead"]["us"] if line and "lmhead" in line else None
+    avg = {c: sum(d[c] for d in runs) / len(runs) for c in MFMA_COUNTERS}
+    gui = avg["GRBM_GUI_ACTIVE"] / N_XCC
+    mops = avg["SQ_INSTS_VALU_MFMA_MOPS_F8"] + avg["SQ_INSTS_VALU_MFMA_MOPS_F6F4"]
+    out = {"workload": workload, "kernel": plan, "kernel_hash": kernel_hash(kname), "dispatches": len(runs),
+           "counters_per_dispatch": avg,
+           "mfma_busy_frac": avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * N_SIMD),
+           "mfma_flops_per_dispatch": mops * 512.0, "algorithmic_flops_per_launch": flops_alg,
+           "kernel_us_in_bench_line": us,
+           "clock_ghz": gui / (us * 1e3) if us else None,
+           "commands": [
+               f"rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv -d gpurun_out/pmcm_{workload} -o run "
+               f"-- python3 bench.py --no-cpu-baseline --no-peaks --no-companions --workload {workload} "
+               f"--steps 5 --warmup 2",
+               f"python3 bench.py --no-cpu-baseline --no-peaks --no-companions --workload {workload} "
+               f"--steps 50 --warmup 5 > gpurun_out/pmcm_{workload}.log",
+               f"python3 bench.py --workload {workload} --summarize-mfma "
+               f"gpurun_out/pmcm_{workload}/run_counter_collection.csv gpurun_out/pmcm_{workload}.log"]}
+    dst = os.path.join(ROOT, "profiles", f"{kname}_{workload}_mfma.json")
     with open(dst, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
@@ -350,9 +406,14 @@ def main() -> int:
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a run with "
                          "--copy-calibration-mib into the traffic summary under profiles/")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_CSV", "BENCH_LOG"),
+                    help="turn a rocprofv3 --pmc CSV of the MFMA counters and a bench log of the same workload "
+                         "into the matrix-core utilisation summary under profiles/")
     args = ap.parse_args()
     global TOPK_K
     TOPK_K = args.topk
+    if args.summarize_mfma:
+        return summarize_mfma(args.workload, *args.summarize_mfma)
     if args.summarize_pmc:
         return summarize_pmc(args.workload, *args.summarize_pmc, args.copy_calibration_mib, args.variant)
 
