@@ -27,7 +27,8 @@
  *
  * Conventions shared by every entry point:
  *   - The caller owns all memory; the library allocates nothing and keeps no
- *     state between calls.
+ *     state between calls, except the device scratch array of
+ *     mtpd_draft_tail_noalloc (and the process-wide plan override).
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
  *     null stream) and never synchronizes.
  *   - Arguments are validated on the host before any HIP call; on failure
@@ -249,7 +250,7 @@ mtpd_status mtpd_fp8_lmhead_topk(const mtpd_qact *act, const int32_t *row_index,
 size_t mtpd_topk_workspace_bytes(int64_t n_rows, int64_t V, int64_t k);
 
 /* Bytes of workspace mtpd_fp8_lmhead_argmax / mtpd_draft_tail need for
- * n_rows output rows (a multiple of 256; 0 for n_rows <= 0). */
+ * n_rows output rows (a multiple of 256; 0 for n_rows <= 0 or above 2^24). */
 size_t mtpd_workspace_bytes(int64_t n_rows);
 
 /* Static name of a status code ("MTPD_OK", ...); "MTPD_UNKNOWN" otherwise. */

@@ -131,12 +131,12 @@ constexpr int kArriveGroups = 32;
 
 inline int workspace_partitions(int64_t n_rows) {
     int P = 256;
-    while (P > 1 && (int64_t)P * n_rows > 4096) P >>= 1;
+    while (P > 1 && n_rows > 4096 / P) P >>= 1;   // P * n_rows > 4096, without overflow
     return P;
 }
 
 inline int workspace_key_stride(int64_t n_rows) {
-    return (int64_t)workspace_partitions(n_rows) * n_rows <= 4096 ? 16 : 1;
+    return n_rows <= 4096 / workspace_partitions(n_rows) ? 16 : 1;
 }
 
 inline size_t workspace_key_bytes(int64_t n_rows) {

@@ -215,7 +215,11 @@ mtpd_status mtpd_set_plan_override(const char* key, const char* value) {
 }
 
 const char* mtpd_status_name(mtpd_status s) {
-    switch (s) {
+    // A C caller may pass any int; in C++ loading an enum object outside the
+    // enumerators' range is undefined, so read its bytes as an int.
+    int v;
+    memcpy(&v, &s, sizeof v);
+    switch (v) {
         case MTPD_OK: return "MTPD_OK";
         case MTPD_ERR_NULL: return "MTPD_ERR_NULL";
         case MTPD_ERR_SHAPE: return "MTPD_ERR_SHAPE";
@@ -261,7 +265,7 @@ const char* mtpd_draft_tail_plan(int64_t M, int64_t V, int64_t H) {
     return buf;
 }
 
-size_t mtpd_workspace_bytes(int64_t n_rows) { return mtpd::workspace_bytes(n_rows); }
+size_t mtpd_workspace_bytes(int64_t n_rows) { return n_rows > kMaxRows ? 0 : mtpd::workspace_bytes(n_rows); }
 
 mtpd_status mtpd_norm_quant(const uint16_t* hidden, const uint16_t* residual, const float* norm_weight, float eps,
                             int64_t M, int64_t H, uint16_t* out_hidden, const mtpd_qact* out_act, void* stream) {
