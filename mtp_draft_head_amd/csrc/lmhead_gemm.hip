@@ -436,6 +436,83 @@ __device__ __forceinline__ void bdma16(rsrc_t r, uint32_t voff, uint32_t soff, v
 // hides a value from constant folding (the zero accumulators of the first block)
 __device__ __forceinline__ void opaque(float& x) { asm volatile("" : "+v"(x)); }
 
+// Row reductions of the epilogue.  The code around them has no branches, so
+// every lane runs every move and a move never reads a disabled lane; the moves
+// are left unpinned so that the compiler folds each into its max or min, and
+// the reductions run breadth first over eight (or four) rows at a time, so that no move
+// waits on the value written just before it.  Controls as for row16_max:
+// lane ^ 1, lane ^ 2, the half-row mirror and the row mirror, all inside a
+// 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_row_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+
+// the order-preserving u32 of a logit (argmax_key's upper word; -0 folds onto
+// +0 through the addition) and back
+__device__ __forceinline__ uint32_t ord_f32(float z) {
+    const uint32_t u = __float_as_uint(z + 0.0f);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ float unord_f32(uint32_t o) {
+    return __uint_as_float(o ^ (~(uint32_t)((int32_t)o >> 31) | 0x80000000u));
+}
+
+// Per-row best of a wave's 16 x 64 sub-tiles, written to LDS: for row group
+// mt and lane row i (row mt * 16 + 4 * (lane / 16) + i), the argmax key of
+// the largest value and the lowest column holding it (columns col0 + lane % 16
+// + 16 nt) goes to dst[mt * 16 + 4 * (lane / 16) + i].  fp32 compares treat -0
+// and +0 as equal, as the key does.
+template <int MT>
+__device__ __forceinline__ void row_best_keys(const float (&acc)[MT][4][4], int lane, uint32_t col0,
+                                              unsigned long long* dst) {
+    constexpr int B = MT % 2 == 0 ? 8 : 4;   // rows per batch: two row groups, or one
+#pragma unroll
+    for (int p0 = 0; p0 < MT * 4; p0 += B) {
+        constexpr int N = B;
+        uint32_t o[N], c[N];
+#pragma unroll
+        for (int q = 0; q < N; ++q) {
+            const int mt = (p0 + q) >> 2, i = (p0 + q) & 3;
+            o[q] = ord_f32(fmaxf(fmaxf(acc[mt][0][i], acc[mt][1][i]), fmaxf(acc[mt][2][i], acc[mt][3][i])));
+        }
+#pragma unroll
+        for (int q = 0; q < N; ++q) o[q] = max(o[q], dpp_row_u32<0xB1>(o[q]));
+#pragma unroll
+        for (int q = 0; q < N; ++q) o[q] = max(o[q], dpp_row_u32<0x4E>(o[q]));
+#pragma unroll
+        for (int q = 0; q < N; ++q) o[q] = max(o[q], dpp_row_u32<0x141>(o[q]));
+#pragma unroll
+        for (int q = 0; q < N; ++q) o[q] = max(o[q], dpp_row_u32<0x140>(o[q]));
+#pragma unroll
+        for (int q = 0; q < N; ++q) {
+            const int mt = (p0 + q) >> 2, i = (p0 + q) & 3;
+            const float rm = unord_f32(o[q]);
+            uint32_t cc = 0x10000u;
+            cc = acc[mt][3][i] == rm ? 48u : cc;
+            cc = acc[mt][2][i] == rm ? 32u : cc;
+            cc = acc[mt][1][i] == rm ? 16u : cc;
+            cc = acc[mt][0][i] == rm ? 0u : cc;
+            c[q] = cc + (uint32_t)(lane & 15);
+        }
+#pragma unroll
+        for (int q = 0; q < N; ++q) c[q] = min(c[q], dpp_row_u32<0xB1>(c[q]));
+#pragma unroll
+        for (int q = 0; q < N; ++q) c[q] = min(c[q], dpp_row_u32<0x4E>(c[q]));
+#pragma unroll
+        for (int q = 0; q < N; ++q) c[q] = min(c[q], dpp_row_u32<0x141>(c[q]));
+#pragma unroll
+        for (int q = 0; q < N; ++q) c[q] = min(c[q], dpp_row_u32<0x140>(c[q]));
+        if ((lane & 15) == 0) {
+#pragma unroll
+            for (int q = 0; q < N; ++q) {
+                const int mt = (p0 + q) >> 2, i = (p0 + q) & 3;
+                dst[mt * 16 + 4 * (lane >> 4) + i] = ((uint64_t)o[q] << 32) | (uint64_t)(0xFFFFFFFFu - (col0 + c[q]));
+            }
+        }
+    }
+}
+
 }  // namespace
 
 template <int MT>
@@ -694,20 +771,7 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
     // compares treat -0 and +0 as equal, as the key does): the 32-bit
     // reductions cost a third of reducing 64-bit keys. ----
     unsigned long long* red = reinterpret_cast<unsigned long long*>(smem);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float v0 = acc[mt][0][i], v1 = acc[mt][1][i], v2 = acc[mt][2][i], v3 = acc[mt][3][i];
-            const float rm = row16_max(fmaxf(fmaxf(v0, v1), fmaxf(v2, v3)));
-            // this lane's columns are lane % 16 + 16 nt, increasing with nt
-            const uint32_t c = v0 == rm ? 0u : (v1 == rm ? 16u : (v2 == rm ? 32u : (v3 == rm ? 48u : 0x10000u)));
-            const uint32_t col = row16_min_u32(c + (uint32_t)(lane & 15));
-            if ((lane & 15) == 0)
-                red[wn * BM + wm * MT * 16 + mt * 16 + 4 * (lane >> 4) + i] =
-                    argmax_key(rm, (uint32_t)(n0 + wn * 64) + col);
-        }
-    }
+    row_best_keys<MT>(acc, lane, (uint32_t)(n0 + wn * 64), red + wn * BM + wm * MT * 16);
     __syncthreads();
     uint64_t old = 0;
     if (t < BM && m0 + t < n_rows) {
