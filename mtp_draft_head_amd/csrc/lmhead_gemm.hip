@@ -439,8 +439,8 @@ __device__ __forceinline__ void opaque(float& x) { asm volatile("" : "+v"(x)); }
 // Row reductions of the epilogue.  The code around them has no branches, so
 // every lane runs every move and a move never reads a disabled lane; the moves
 // are left unpinned so that the compiler folds each into its max or min, and
-// the reductions run breadth first over eight (or four) rows at a time, so that no move
-// waits on the value written just before it.  Controls as for row16_max:
+// the reductions run breadth first over eight (or four) rows at a time, so
+// that no move waits on the value written just before it.  Controls as for row16_max:
 // lane ^ 1, lane ^ 2, the half-row mirror and the row mirror, all inside a
 // 16-lane row.
 template <int CTRL>
@@ -449,52 +449,52 @@ __device__ __forceinline__ uint32_t dpp_row_u32(uint32_t v) {
 }
 
 // the order-preserving u32 of a logit (argmax_key's upper word; -0 folds onto
-// +0 through the addition) and back
+// +0 through the addition)
 __device__ __forceinline__ uint32_t ord_f32(float z) {
     const uint32_t u = __float_as_uint(z + 0.0f);
     return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-}
-__device__ __forceinline__ float unord_f32(uint32_t o) {
-    return __uint_as_float(o ^ (~(uint32_t)((int32_t)o >> 31) | 0x80000000u));
 }
 
 // Per-row best of a wave's 16 x 64 sub-tiles, written to LDS: for row group
 // mt and lane row i (row mt * 16 + 4 * (lane / 16) + i), the argmax key of
 // the largest value and the lowest column holding it (columns col0 + lane % 16
-// + 16 nt) goes to dst[mt * 16 + 4 * (lane / 16) + i].  fp32 compares treat -0
-// and +0 as equal, as the key does.
+// + 16 nt) goes to dst[mt * 16 + 4 * (lane / 16) + i].  Each lane first finds
+// its largest value and the lowest of its four columns holding it; the row's
+// maximum over the 16 lanes follows as an ordered u32, and the lowest column
+// among the lanes whose maximum equals it.  fp32 compares (and the ordered
+// u32, which folds -0 onto +0) treat -0 and +0 as equal, as the key does.
 template <int MT>
 __device__ __forceinline__ void row_best_keys(const float (&acc)[MT][4][4], int lane, uint32_t col0,
                                               unsigned long long* dst) {
-    constexpr int B = MT % 2 == 0 ? 8 : 4;   // rows per batch: two row groups, or one
+    constexpr int B = MT % 2 == 0 ? 8 : 4;
+    const uint32_t l16 = (uint32_t)(lane & 15);
 #pragma unroll
     for (int p0 = 0; p0 < MT * 4; p0 += B) {
         constexpr int N = B;
-        uint32_t o[N], c[N];
+        uint32_t o[N], om[N], c[N];
 #pragma unroll
         for (int q = 0; q < N; ++q) {
             const int mt = (p0 + q) >> 2, i = (p0 + q) & 3;
-            o[q] = ord_f32(fmaxf(fmaxf(acc[mt][0][i], acc[mt][1][i]), fmaxf(acc[mt][2][i], acc[mt][3][i])));
+            const float v0 = acc[mt][0][i], v1 = acc[mt][1][i], v2 = acc[mt][2][i], v3 = acc[mt][3][i];
+            const float m = fmaxf(fmaxf(v0, v1), fmaxf(v2, v3));
+            uint32_t cc = l16 + 48u;
+            cc = v2 == m ? l16 + 32u : cc;
+            cc = v1 == m ? l16 + 16u : cc;
+            cc = v0 == m ? l16 : cc;
+            c[q] = cc;
+            o[q] = ord_f32(m);
+            om[q] = o[q];
         }
 #pragma unroll
-        for (int q = 0; q < N; ++q) o[q] = max(o[q], dpp_row_u32<0xB1>(o[q]));
+        for (int q = 0; q < N; ++q) om[q] = max(om[q], dpp_row_u32<0xB1>(om[q]));
 #pragma unroll
-        for (int q = 0; q < N; ++q) o[q] = max(o[q], dpp_row_u32<0x4E>(o[q]));
+        for (int q = 0; q < N; ++q) om[q] = max(om[q], dpp_row_u32<0x4E>(om[q]));
 #pragma unroll
-        for (int q = 0; q < N; ++q) o[q] = max(o[q], dpp_row_u32<0x141>(o[q]));
+        for (int q = 0; q < N; ++q) om[q] = max(om[q], dpp_row_u32<0x141>(om[q]));
 #pragma unroll
-        for (int q = 0; q < N; ++q) o[q] = max(o[q], dpp_row_u32<0x140>(o[q]));
+        for (int q = 0; q < N; ++q) om[q] = max(om[q], dpp_row_u32<0x140>(om[q]));
 #pragma unroll
-        for (int q = 0; q < N; ++q) {
-            const int mt = (p0 + q) >> 2, i = (p0 + q) & 3;
-            const float rm = unord_f32(o[q]);
-            uint32_t cc = 0x10000u;
-            cc = acc[mt][3][i] == rm ? 48u : cc;
-            cc = acc[mt][2][i] == rm ? 32u : cc;
-            cc = acc[mt][1][i] == rm ? 16u : cc;
-            cc = acc[mt][0][i] == rm ? 0u : cc;
-            c[q] = cc + (uint32_t)(lane & 15);
-        }
+        for (int q = 0; q < N; ++q) c[q] = o[q] == om[q] ? c[q] : 0x10000u;
 #pragma unroll
         for (int q = 0; q < N; ++q) c[q] = min(c[q], dpp_row_u32<0xB1>(c[q]));
 #pragma unroll
@@ -507,7 +507,7 @@ __device__ __forceinline__ void row_best_keys(const float (&acc)[MT][4][4], int 
 #pragma unroll
             for (int q = 0; q < N; ++q) {
                 const int mt = (p0 + q) >> 2, i = (p0 + q) & 3;
-                dst[mt * 16 + 4 * (lane >> 4) + i] = ((uint64_t)o[q] << 32) | (uint64_t)(0xFFFFFFFFu - (col0 + c[q]));
+                dst[mt * 16 + 4 * (lane >> 4) + i] = ((uint64_t)om[q] << 32) | (uint64_t)(0xFFFFFFFFu - (col0 + c[q]));
             }
         }
     }
