@@ -54,6 +54,11 @@ struct LmheadArgs {
 
 hipError_t launch_lmhead_argmax(const LmheadArgs& a, hipStream_t stream);
 
+// one packed row: the persistent one-row kernel of the fused tail as the LM
+// head alone
+bool use_lmhead1(const LmheadArgs& a);
+hipError_t launch_lmhead1(const LmheadArgs& a, hipStream_t stream);
+
 // name and launch shape of the kernel launch_lmhead_argmax picks
 void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len);
 

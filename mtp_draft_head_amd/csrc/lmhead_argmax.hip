@@ -452,6 +452,18 @@ void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len
         describe_gemm(n_rows, V, H, n_rows, buf, len);
         return;
     }
+    {
+        LmheadArgs a1{};
+        a1.n_rows = n_rows;
+        a1.a_rows = n_rows;
+        a1.V = V;
+        a1.H = H;
+        if (use_lmhead1(a1)) {
+            snprintf(buf, len, "draft_tail1_kernel (LM head only) grid=%lldx256 (%lld tiles)",
+                     (long long)draft_tail1_grid(V), (long long)(V / 16));
+            return;
+        }
+    }
     StreamTile st;
     if (use_stream(n_rows, V, H, n_rows, &st)) {
         snprintf(buf, len, "lmhead_stream_kernel<%d,%d,%d> grid=%lldx64", st.nt, st.ma, st.d,
@@ -484,6 +496,7 @@ void describe_lmhead(int64_t n_rows, int64_t V, int64_t H, char* buf, size_t len
 
 hipError_t launch_lmhead_argmax(const LmheadArgs& a, hipStream_t stream) {
     if (use_gemm(a.n_rows, a.V, a.H, a.a_rows)) return launch_lmhead_gemm(a, stream);
+    if (use_lmhead1(a)) return launch_lmhead1(a, stream);
     StreamTile st;
     if (use_stream(a.n_rows, a.V, a.H, a.a_rows, &st)) return launch_lmhead_stream(a, st.nt, st.ma, st.d, stream);
     RowsTile rt;

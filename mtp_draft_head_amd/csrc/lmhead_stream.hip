@@ -1212,6 +1212,10 @@ hipError_t launch_lmhead_topk(const LmheadArgs& a, int k, float* out_val, int32_
 // before the weight ring, so the norm waits only for them while the ring
 // fills (the vector-memory counter is in order).  Workgroup 0 writes the
 // row's outputs after its stream.
+//
+// The same kernel is the LM head alone for one packed row (hidden == NULL):
+// the row's codes and scales reach LDS by direct copies in place of the norm
+// inputs, and nothing but the (max, index) pair is written.
 // ---------------------------------------------------------------------------
 
 constexpr int kTail1MaxH = 6144;   // NSTEP <= 3 steps of 2048 columns
@@ -1223,7 +1227,9 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
     const float* __restrict__ gamma, float eps, int H,
     const uint8_t* __restrict__ w_codes, const float* __restrict__ w_scales, int total_tiles,
     uint16_t* __restrict__ out_hidden, uint8_t* __restrict__ codes, float* __restrict__ scales,
-    float* __restrict__ out_max, int32_t* __restrict__ out_idx, ArgmaxWs ws)
+    float* __restrict__ out_max, int32_t* __restrict__ out_idx, ArgmaxWs ws,
+    const uint8_t* __restrict__ act_codes, const float* __restrict__ act_scales,
+    const int32_t* __restrict__ row_index)
 {
     constexpr int D = kTail1D;
     constexpr int SLOT = 2 * 64;             // one 16-row weight tile (uint4s)
@@ -1251,9 +1257,12 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
     const int KB = H >> 7;
     const int G = (int)gridDim.x;
     const int b = (int)blockIdx.x;
+    const bool fused = hidden != nullptr;   // else the LM head alone on a packed row
     const int ntiles = (total_tiles - b + G - 1) / G;   // this workgroup's tiles: b, b + G, ...
     // this wave's K blocks of every tile [kb0, kb1); every wave walks NBU
-    // units per tile (units past its range are dead: zero factor)
+    // units per tile (units past its range are dead: zero factor).  With
+    // fewer than four K blocks some waves own none (nb = 0): their units read
+    // block kb0 (< KB, real data, so the dead partial is a finite zero)
     const int kb0 = (wave * KB) >> 2, kb1 = ((wave + 1) * KB) >> 2;
     const int nb = kb1 - kb0;
     const int NBU = (KB + 3) >> 2;
@@ -1275,7 +1284,7 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
     auto refill = [&](int slot, int u) {
         const int uc = min(u, nunits - 1);
         const int i = uc / NBU, j = uc - i * NBU;
-        const int kb = kb0 + min(j, nb - 1);
+        const int kb = kb0 + max(min(j, nb - 1), 0);
         const uint8_t* wb = w_codes + (size_t)(b + i * G) * 16 * (size_t)H + (size_t)kb * kBlock;
 #pragma unroll
         for (int q = 0; q < 2; ++q) lds_copy16_stream(wb, woff[q], ring0 + (uint32_t)(slot * SLOT + q * 64) * 16u);
@@ -1285,15 +1294,28 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
     //    columns k*2048 + 8t, clamped into the row), the weight-scale rows of
     //    the workgroup's tiles (first and last tile's row span, lanes past KB
     //    idle), then the first D-1 units of the ring
+    if (fused) {
 #pragma unroll
-    for (int k = 0; k < NSTEP; ++k) {
-        const uint32_t cc = (uint32_t)min(k * 2048 + t * 8, H - 8);
-        const uint32_t dst = (uint32_t)(k * 256 + wave * 64) * 16u;
-        lds_copy16(reinterpret_cast<const uint8_t*>(hidden), cc * 2u, lds_addr(h_lds) + dst);
-        lds_copy16(reinterpret_cast<const uint8_t*>(residual), cc * 2u, lds_addr(r_lds) + dst);
-        lds_copy16(reinterpret_cast<const uint8_t*>(gamma), cc * 4u, lds_addr(g_lds) + (uint32_t)((k * 2 * 256) + wave * 64) * 16u);
-        lds_copy16(reinterpret_cast<const uint8_t*>(gamma), cc * 4u + 16u,
-                   lds_addr(g_lds) + (uint32_t)((k * 2 + 1) * 256 + wave * 64) * 16u);
+        for (int k = 0; k < NSTEP; ++k) {
+            const uint32_t cc = (uint32_t)min(k * 2048 + t * 8, H - 8);
+            const uint32_t dst = (uint32_t)(k * 256 + wave * 64) * 16u;
+            lds_copy16(reinterpret_cast<const uint8_t*>(hidden), cc * 2u, lds_addr(h_lds) + dst);
+            lds_copy16(reinterpret_cast<const uint8_t*>(residual), cc * 2u, lds_addr(r_lds) + dst);
+            lds_copy16(reinterpret_cast<const uint8_t*>(gamma), cc * 4u,
+                       lds_addr(g_lds) + (uint32_t)((k * 2 * 256) + wave * 64) * 16u);
+            lds_copy16(reinterpret_cast<const uint8_t*>(gamma), cc * 4u + 16u,
+                       lds_addr(g_lds) + (uint32_t)((k * 2 + 1) * 256 + wave * 64) * 16u);
+        }
+    } else {
+        // the packed row: thread t's 16-byte pieces at 4096 k + 16 t, and the
+        // row's scales (wave 0; lanes past KB repeat the last)
+        const int arow = row_index ? row_index[0] : 0;
+        const uint8_t* ac = act_codes + (size_t)arow * (size_t)H;
+        for (int k = 0; k * 4096 < H; ++k)
+            if (k * 4096 + t * 16 < H)
+                lds_copy16(ac, (uint32_t)(k * 4096 + t * 16), lds_addr(a_lds) + (uint32_t)(k * 256 + wave * 64) * 16u);
+        if (wave == 0)
+            lds_copy4(act_scales + (size_t)arow * KB, (uint32_t)min(lane, KB - 1) * 4u, lds_addr(sa_lds));
     }
     // weight-scale rows: tile b + i*G lies in row ((b + i*G) * 16) >> 7;
     // slot i holds tile i's row (the host keeps ntiles <= kTail1MaxTiles)
@@ -1304,13 +1326,16 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
 #pragma unroll
     for (int s2 = 0; s2 < D - 1; ++s2) refill(s2, rq++);
 
-    // 2. wait for this wave's norm copies only (the sw rows and the ring stay
-    //    in flight), then all waves' (barrier), then norm_quant_kernel's body
+    // 2. wait for this wave's norm (or packed-row) copies only (the sw rows
+    //    and the ring stay in flight), then all waves' (barrier), then
+    //    norm_quant_kernel's body
     {
         const int nsw = (ntiles - wave + 3) / 4;   // this wave's weight-scale copies
         wait_vm(max(nsw, 0) + (D - 1) * PER_BLOCK);
     }
     __syncthreads();
+    float y[NSTEP][8];
+    if (fused) {
     float sv[NSTEP][8];
     float4 graw[NSTEP][2];
 #pragma unroll
@@ -1341,7 +1366,6 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
 
     // every group computed (columns past H hold s = 0; they fill whole
     // 128-column blocks, which are not stored)
-    float y[NSTEP][8];
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k) {
         const float4 g0 = graw[k][0], g1 = graw[k][1];
@@ -1360,6 +1384,7 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
         if ((t & 15) == 0) sa_lds[c >> 7] = bscale[k];
     }
     __syncthreads();
+    }
 
     // 3. the weight stream: every unit's fragment rows all read the packed
     //    row; at each tile end the four partials meet in LDS (double-buffered
@@ -1373,7 +1398,7 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
     float pf = 0.f;
     auto compute = [&](int slot) {
         const bool live = ci < ntiles && cj < nb;
-        const int kb = kb0 + min(cj, nb - 1);
+        const int kb = kb0 + max(min(cj, nb - 1), 0);
         const float swv = sw_lds[min(ci, ntiles - 1)][kb];
         const float f = sa_lds[kb] * (live ? swv : 0.f);
         const uint4 a0 = *reinterpret_cast<const uint4*>(&a_lds[kb * kBlock + fg * 16]);
@@ -1412,7 +1437,7 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
     MTPD_WAIT_VM(0);   // the clamped tail refills, before LDS is reused
 
     // 4. outputs of the row (workgroup 0), the row's best key, arrival
-    if (b == 0) {
+    if (fused && b == 0) {
 #pragma unroll
         for (int k = 0; k < NSTEP; ++k) {
             const int c = k * 2048 + t * 8;
@@ -1455,7 +1480,24 @@ hipError_t launch_draft_tail1(const uint16_t* hidden, const uint16_t* residual, 
     const int64_t grid = draft_tail1_grid(V);
     hipLaunchKernelGGL(draft_tail1_kernel, dim3((unsigned)grid), dim3(256), 0, stream, hidden, residual, gamma, eps,
                        (int)H, w_codes, w_scales, (int)tiles, out_hidden, codes, scales, out_max, out_idx,
-                       argmax_ws(workspace, 1));
+                       argmax_ws(workspace, 1), nullptr, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+bool use_lmhead1(const LmheadArgs& a) {
+    // the persistent one-row kernel, unless a test pins another shape
+    const PlanOverride& po = plan_override();
+    return a.n_rows == 1 && a.H <= kTail1MaxH && po.lmhead_kernel == 0 && po.stream[0] == 0 &&
+           !po.draft_tail_split;
+}
+
+hipError_t launch_lmhead1(const LmheadArgs& a, hipStream_t stream) {
+    const int64_t tiles = a.V / 16;
+    if (tiles > 0x7FFFFFFF || a.H > kTail1MaxH || a.n_rows != 1) return hipErrorInvalidValue;
+    const int64_t grid = draft_tail1_grid(a.V);
+    hipLaunchKernelGGL(draft_tail1_kernel, dim3((unsigned)grid), dim3(256), 0, stream, nullptr, nullptr, nullptr, 0.f,
+                       (int)a.H, a.w_codes, a.w_scales, (int)tiles, nullptr, nullptr, nullptr, a.out_max, a.out_idx,
+                       argmax_ws(a.workspace, 1), a.a_codes, a.a_scales, a.row_index);
     return hipGetLastError();
 }
 

@@ -331,8 +331,8 @@ def test_stream_rows_kernel_vocab_shard_shape(workloads):
 
 # 16-row tiles per workgroup: one (256, 2048, 4096), one or two (5120), four
 # or five (18944), eight or nine (33152), sixteen on 592 workgroups (151552)
-@pytest.mark.parametrize("H,V", [(128, 256), (1152, 2048), (2304, 4096), (1152, 5120), (6144, 18944),
-                                 (640, 33152), (2048, 151552)])
+@pytest.mark.parametrize("H,V", [(128, 256), (256, 512), (384, 640), (1152, 2048), (2304, 4096), (1152, 5120),
+                                 (6144, 18944), (640, 33152), (2048, 151552)])
 def test_fused_one_row_draft_tail_matches_split(H, V):
     """One row: the fused single-kernel tail reproduces the two-launch path's
     recycled hidden, codes and scales bit for bit (the same arithmetic), and
@@ -350,6 +350,29 @@ def test_fused_one_row_draft_tail_matches_split(H, V):
     check_norm_quant(d, *fused[:3])
     check_lmhead(fused[1], fused[2], d, fused[3], fused[4])
     check_lmhead(split[1], split[2], d, split[3], split[4])
+
+
+# H = 128 .. 384: fewer K blocks than waves (a wave with none must still
+# read real data: a dead unit's zero factor times NaN would poison the row)
+@pytest.mark.parametrize("H,V", [(128, 256), (256, 512), (384, 640), (1152, 5120), (6144, 18944), (2048, 151552)])
+def test_one_row_lm_head_alone(H, V):
+    """The LM head alone on one packed row runs the fused tail's persistent
+    kernel: its (max, index) equal the fused tail's bit for bit, meet the
+    oracle, and a gathered row (row_index into a 3-row activation) gives that
+    row's pair."""
+    say(f"one-row head H={H} V={V}: {mtpd.lmhead_plan(1, V, H)}")
+    assert mtpd.lmhead_plan(1, V, H).startswith("draft_tail1_kernel")
+    d = inputs.random_case(43 + H, 3, H, V, outliers=True)
+    h, r, g, wc, ws = to_dev(d)
+    _, codes, scales, _, _ = mtpd.draft_tail(h, r, g, d["eps"], wc, ws)
+    fused = mtpd.draft_tail(h[2:3], r[2:3], g, d["eps"], wc, ws)
+    m, i = mtpd.fp8_lmhead_argmax(codes[2:3].contiguous(), scales[2:3].contiguous(), wc, ws)
+    idx = torch.tensor([2], dtype=torch.int32, device=DEV)
+    mg, ig = mtpd.fp8_lmhead_argmax(codes, scales, wc, ws, row_index=idx)
+    torch.cuda.synchronize()
+    assert torch.equal(m, fused[3]) and torch.equal(i, fused[4])
+    assert torch.equal(mg, m) and torch.equal(ig, i)
+    check_lmhead(fused[1], fused[2], d, m, i)
 
 
 def _scaled_case(seed, M, H, V, row_mag, small_blocks=()):
