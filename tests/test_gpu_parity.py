@@ -375,6 +375,44 @@ def test_one_row_lm_head_alone(H, V):
     check_lmhead(fused[1], fused[2], d, m, i)
 
 
+# one shape per kernel family: fused one-row tail, per-tile stream, rows
+# kernel, K-outer kernel, compute-regime tile
+@pytest.mark.parametrize("M,H,V", [(1, 512, 2048), (8, 512, 2048), (40, 256, 4096), (64, 256, 151552),
+                                   (300, 256, 1024)])
+def test_workspace_canaries(M, H, V):
+    """The kernels touch only the workspace they are given and leave it zero:
+    4 KB guard regions of 0xA5 on both sides of it stay intact, twice."""
+    import ctypes
+    from mtp_draft_head_amd import FP8Weight, QAct
+
+    d = inputs.random_case(47 + M, M, H, V)
+    h, r, g, wc, ws = to_dev(d)
+    L = mtpd.lib()
+    need = L.mtpd_workspace_bytes(M)
+    G = 4096
+    buf = torch.zeros(G + need + G, dtype=torch.uint8, device=DEV)
+    buf[:G] = 0xA5
+    buf[G + need:] = 0xA5
+    out_h = torch.empty((M, H), dtype=torch.bfloat16, device=DEV)
+    codes = torch.empty((M, H), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((M, H // 128), dtype=torch.float32, device=DEV)
+    om = torch.empty((M,), dtype=torch.float32, device=DEV)
+    oi = torch.empty((M,), dtype=torch.int32, device=DEV)
+    qa = QAct(codes.data_ptr(), scales.data_ptr(), M, H)
+    w = FP8Weight(wc.data_ptr(), ws.data_ptr(), V, H)
+    ref = mtpd.draft_tail(h, r, g, d["eps"], wc, ws)
+    for _ in range(2):
+        st = L.mtpd_draft_tail(h.data_ptr(), r.data_ptr(), g.data_ptr(), float(d["eps"]), M, H, ctypes.byref(w),
+                               out_h.data_ptr(), ctypes.byref(qa), om.data_ptr(), oi.data_ptr(),
+                               buf.data_ptr() + G, need, torch.cuda.current_stream(DEV).cuda_stream)
+        assert st == 0, L.mtpd_last_error().decode()
+        torch.cuda.synchronize()
+        assert bool((buf[:G] == 0xA5).all()) and bool((buf[G + need:] == 0xA5).all())
+        assert int(buf[G:G + need].count_nonzero()) == 0
+        assert torch.equal(oi, ref[4]) and torch.equal(om, ref[3])
+    say(f"  canaries M={M} H={H} V={V}: {mtpd.draft_tail_plan(M, V, H)}")
+
+
 def _scaled_case(seed, M, H, V, row_mag, small_blocks=()):
     """random_case with row m of hidden and residual scaled by row_mag[m], and
     the listed (row, 128-column block) pairs 1e-30 times smaller still."""
