@@ -293,7 +293,10 @@ __global__ __launch_bounds__(512) void lmhead_gemm_kernel(
 //
 //  - BM = 32 * MT activation rows x 256 vocab rows per workgroup (8 waves,
 //    2 x 4, each 16 * MT rows x 64 columns).  MT = 8 gives 256-row tiles;
-//    MT = 5 gives 160-row tiles, whose height divides 320 rows exactly.
+//    MT = 5 160-row tiles; MT = 10 320-row tiles (257 to 320 rows in one
+//    tile, so each weight tile is copied once).  Row tiles go in groups of
+//    `group_rows`, row fastest inside a group, consecutive ids on one XCD:
+//    with groups of 8 an XCD's 32 workgroups cover 8 row x 4 column tiles.
 //  - Staging: per K block both operand tiles go global -> LDS as [row][128
 //    bytes], eight consecutive lanes per row's 128 bytes (a whole cache line
 //    per eight lanes: measured 12.4 against 10.7 TB/s of L2 -> LDS for four
