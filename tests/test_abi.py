@@ -278,3 +278,15 @@ def test_noalloc_rejects_too_many_rows(L):
     assert st == 5, st   # MTPD_ERR_WORKSPACE, before any HIP call
     assert "65536" in L.mtpd_last_error().decode()
     L.mtpd_clear_error()
+
+
+def test_dispatcher_sweep_reaches_every_kernel_family():
+    """The GPU dispatcher sweep is only as good as the kernels it reaches
+    (the plan is decided on the host, so this runs without a GPU)."""
+    from tests.test_gpu_parity import SWEEP
+    fams = set()
+    for M, H, V, cus, _, _ in SWEEP:
+        with m.plan_override(**({"device_cus": cus} if cus else {})):
+            fams.add(m.lmhead_plan(M, V, H).split("<")[0].split(" ")[0])
+    assert {"draft_tail1_kernel", "lmhead_stream_kernel", "lmhead_stream_rows_kernel", "lmhead_kouter_kernel",
+            "lmhead_gemm2_kernel", "lmhead_argmax_kernel"} <= fams, fams

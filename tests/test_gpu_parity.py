@@ -515,6 +515,57 @@ def _sample(M, n, must, seed):
     return np.array(sorted(rows), np.int32)
 
 
+def _sweep_cases(n=28, seed=20261202, cap=1.5e9):
+    """Seeded shapes across every kernel family the dispatcher holds: row
+    counts on both sides of each boundary (1, 16/17, 64/65, 256/257), H up to
+    past the streaming kernels' limit, V a multiple of 128 or of 256, and
+    sometimes a small CU count (which turns small vocabularies into several
+    tiles per workgroup)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.choice([1, 2, 5, 9, 16, 17, 31, 33, 48, 64, 65, 100, 129, 200, 257, 300]))
+        H = 128 * int(rng.integers(1, 73))
+        V = (256 if rng.random() < 0.5 else 128) * int(rng.integers(1, 33))
+        cus = [None, None, 8, 37][int(rng.integers(0, 4))]
+        gather = bool(rng.random() < 0.5)
+        if M * H * V <= cap:
+            out.append((M, H, V, cus, gather, int(rng.integers(0, 2 ** 31))))
+    # and the families a random draw may miss: the one-row tail and the
+    # K-outer kernel (several tiles per workgroup) in both of its shapes
+    out += [(1, 2048, 4096, None, True, 11), (1, 6144, 2560, 8, False, 12),
+            (48, 1024, 4608, 8, True, 13), (40, 768, 4096, 8, False, 14), (64, 2304, 5120, 8, True, 15)]
+    return out
+
+
+SWEEP = _sweep_cases()
+
+
+@pytest.mark.parametrize("M,H,V,cus,gather,seed", SWEEP)
+def test_dispatcher_sweep(M, H, V, cus, gather, seed):
+    """Whatever kernel the dispatcher picks: the norm step on every row, the
+    packed activation self-consistent, every row's argmax against the oracle;
+    half the cases also run the LM head alone on a gathered, repeating row
+    list and check that against the oracle."""
+    with mtpd.plan_override(**({"device_cus": cus} if cus else {})):
+        say(f"sweep M={M} H={H} V={V} cus={cus} gather={gather}: {mtpd.lmhead_plan(M, V, H)}")
+        d = inputs.random_case(seed, M, H, V, outliers=True)
+        h, r, g, wc, ws = to_dev(d)
+        out_h, codes, scales, gmax, gidx = mtpd.draft_tail(h, r, g, d["eps"], wc, ws)
+        if gather:
+            n = int(np.random.default_rng(seed).integers(1, M + 6))
+            sel = np.random.default_rng(seed + 1).integers(0, M, n).astype(np.int32)
+            idx = torch.from_numpy(sel).to(DEV)
+            say(f"  gathered {n} rows: {mtpd.lmhead_plan(n, V, H)}")
+            mg, ig = mtpd.fp8_lmhead_argmax(codes, scales, wc, ws, row_index=idx)
+    check_norm_quant(d, out_h, codes, scales)
+    check_self_consistent(codes, scales)
+    say("  " + str(check_lmhead(codes, scales, d, gmax, gidx)))
+    if gather:
+        il = idx.long()
+        say("  gathered " + str(check_lmhead(codes[il], scales[il], d, mg, ig)))
+
+
 @pytest.mark.parametrize("name", ["decode_c1_tp8_shard", "decode_c64_full", "mtp5_batch", "compute_stress"])
 def test_workload_full_size(name, workloads):
     d = workloads(name)
