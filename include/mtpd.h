@@ -142,7 +142,7 @@ mtpd_status mtpd_fp8_lmhead_argmax(const mtpd_qact *act, const int32_t *row_inde
  * argmax of "[Spec Decode][Perf] Fuse the MTP trailing all-reduce;
  * local-argmax draft tokens", Summary.  Same arguments, layouts, workspace
  * contract and results as the two calls in sequence; w->H must equal H.
- * One row with H <= 6144 runs as a single fused launch whose recycled
+ * One row with H <= 8192 runs as a single fused launch whose recycled
  * hidden, codes and scales are bit-identical to the two-launch path.
  */
 mtpd_status mtpd_draft_tail(const uint16_t *hidden, const uint16_t *residual,

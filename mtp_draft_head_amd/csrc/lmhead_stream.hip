@@ -1218,10 +1218,15 @@ hipError_t launch_lmhead_topk(const LmheadArgs& a, int k, float* out_val, int32_
 // inputs, and nothing but the (max, index) pair is written.
 // ---------------------------------------------------------------------------
 
-constexpr int kTail1MaxH = 6144;   // NSTEP <= 3 steps of 2048 columns
+constexpr int kTail1MaxH = 8192;   // NSTEP <= 4 steps of 2048 columns
 constexpr int kTail1D = 6;         // ring depth per wave
 constexpr int kTail1MaxTiles = 16; // tiles per workgroup (one staged weight-scale row each)
 
+// NSTEP 2048-column steps of the norm (3 up to H = 6144, 4 up to 8192): the
+// step count of norm_quant_kernel for that H or more, whose extra steps hold
+// s = 0 and add exact zeros to the sum of squares, so the norm stays
+// bit-identical to the two-launch path
+template <int NSTEP>
 __global__ __launch_bounds__(256) void draft_tail1_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ residual,
     const float* __restrict__ gamma, float eps, int H,
@@ -1234,7 +1239,7 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
     constexpr int D = kTail1D;
     constexpr int SLOT = 2 * 64;             // one 16-row weight tile (uint4s)
     constexpr int PER_BLOCK = 2;
-    constexpr int NSTEP = (kTail1MaxH + 2047) / 2048;
+    static_assert(NSTEP * 2048 <= kTail1MaxH, "the norm's steps cover at most kTail1MaxH columns");
     static_assert((D - 1) * PER_BLOCK <= 63, "vmcnt holds at most 63");
     __shared__ __align__(16) uint4 ring[4][D * SLOT];
     // norm inputs as copied: per step k, hidden and residual in column order;
@@ -1243,7 +1248,7 @@ __global__ __launch_bounds__(256) void draft_tail1_kernel(
     __shared__ __align__(16) uint4 h_lds[NSTEP * 256];
     __shared__ __align__(16) uint4 r_lds[NSTEP * 256];
     __shared__ __align__(16) uint4 g_lds[NSTEP * 2 * 256];
-    __shared__ __align__(16) uint8_t a_lds[kTail1MaxH];
+    __shared__ __align__(16) uint8_t a_lds[NSTEP * 2048];
     __shared__ __align__(16) float sa_lds[kStreamMaxKB];
     __shared__ __align__(16) float sw_lds[kTail1MaxTiles][kStreamMaxKB];
     __shared__ float part[2][4][16];
@@ -1478,9 +1483,14 @@ hipError_t launch_draft_tail1(const uint16_t* hidden, const uint16_t* residual, 
     const int64_t tiles = V / 16;
     if (tiles > 0x7FFFFFFF || H > kTail1MaxH) return hipErrorInvalidValue;
     const int64_t grid = draft_tail1_grid(V);
-    hipLaunchKernelGGL(draft_tail1_kernel, dim3((unsigned)grid), dim3(256), 0, stream, hidden, residual, gamma, eps,
-                       (int)H, w_codes, w_scales, (int)tiles, out_hidden, codes, scales, out_max, out_idx,
-                       argmax_ws(workspace, 1), nullptr, nullptr, nullptr);
+    if (H <= 6144)
+        hipLaunchKernelGGL(draft_tail1_kernel<3>, dim3((unsigned)grid), dim3(256), 0, stream, hidden, residual, gamma,
+                           eps, (int)H, w_codes, w_scales, (int)tiles, out_hidden, codes, scales, out_max, out_idx,
+                           argmax_ws(workspace, 1), nullptr, nullptr, nullptr);
+    else
+        hipLaunchKernelGGL(draft_tail1_kernel<4>, dim3((unsigned)grid), dim3(256), 0, stream, hidden, residual, gamma,
+                           eps, (int)H, w_codes, w_scales, (int)tiles, out_hidden, codes, scales, out_max, out_idx,
+                           argmax_ws(workspace, 1), nullptr, nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -1495,9 +1505,14 @@ hipError_t launch_lmhead1(const LmheadArgs& a, hipStream_t stream) {
     const int64_t tiles = a.V / 16;
     if (tiles > 0x7FFFFFFF || a.H > kTail1MaxH || a.n_rows != 1) return hipErrorInvalidValue;
     const int64_t grid = draft_tail1_grid(a.V);
-    hipLaunchKernelGGL(draft_tail1_kernel, dim3((unsigned)grid), dim3(256), 0, stream, nullptr, nullptr, nullptr, 0.f,
-                       (int)a.H, a.w_codes, a.w_scales, (int)tiles, nullptr, nullptr, nullptr, a.out_max, a.out_idx,
-                       argmax_ws(a.workspace, 1), a.a_codes, a.a_scales, a.row_index);
+    if (a.H <= 6144)
+        hipLaunchKernelGGL(draft_tail1_kernel<3>, dim3((unsigned)grid), dim3(256), 0, stream, nullptr, nullptr, nullptr,
+                           0.f, (int)a.H, a.w_codes, a.w_scales, (int)tiles, nullptr, nullptr, nullptr, a.out_max,
+                           a.out_idx, argmax_ws(a.workspace, 1), a.a_codes, a.a_scales, a.row_index);
+    else
+        hipLaunchKernelGGL(draft_tail1_kernel<4>, dim3((unsigned)grid), dim3(256), 0, stream, nullptr, nullptr, nullptr,
+                           0.f, (int)a.H, a.w_codes, a.w_scales, (int)tiles, nullptr, nullptr, nullptr, a.out_max,
+                           a.out_idx, argmax_ws(a.workspace, 1), a.a_codes, a.a_scales, a.row_index);
     return hipGetLastError();
 }
 

@@ -88,7 +88,7 @@ def check_lmhead(codes, scales, d, gmax, gidx, rows=None):
 
 SHAPES = [
     (1, 128, 128), (4, 256, 1024), (5, 384, 640), (17, 640, 1152), (33, 1024, 384),
-    (64, 2048, 2048), (65, 768, 256), (130, 256, 512), (3, 16384, 256), (2, 6144, 2304),
+    (64, 2048, 2048), (65, 768, 256), (130, 256, 512), (3, 16384, 256), (2, 6144, 2304), (1, 8320, 256),
 ]
 
 
@@ -331,8 +331,11 @@ def test_stream_rows_kernel_vocab_shard_shape(workloads):
 
 # 16-row tiles per workgroup: one (256, 2048, 4096), one or two (5120), four
 # or five (18944), eight or nine (33152), sixteen on 592 workgroups (151552)
+# H past 6144 runs the norm in four 2048-column steps (6272: a partial fourth
+# step; 7168 x 16256: one GPU's eighth of a 129280-row vocab, padded to 128-row blocks)
 @pytest.mark.parametrize("H,V", [(128, 256), (256, 512), (384, 640), (1152, 2048), (2304, 4096), (1152, 5120),
-                                 (6144, 18944), (640, 33152), (2048, 151552)])
+                                 (6144, 18944), (640, 33152), (2048, 151552), (6272, 2048), (7168, 16256),
+                                 (8192, 4096)])
 def test_fused_one_row_draft_tail_matches_split(H, V):
     """One row: the fused single-kernel tail reproduces the two-launch path's
     recycled hidden, codes and scales bit for bit (the same arithmetic), and
@@ -354,7 +357,8 @@ def test_fused_one_row_draft_tail_matches_split(H, V):
 
 # H = 128 .. 384: fewer K blocks than waves (a wave with none must still
 # read real data: a dead unit's zero factor times NaN would poison the row)
-@pytest.mark.parametrize("H,V", [(128, 256), (256, 512), (384, 640), (1152, 5120), (6144, 18944), (2048, 151552)])
+@pytest.mark.parametrize("H,V", [(128, 256), (256, 512), (384, 640), (1152, 5120), (6144, 18944), (2048, 151552),
+                                 (7168, 16256), (8192, 2048)])
 def test_one_row_lm_head_alone(H, V):
     """The LM head alone on one packed row runs the fused tail's persistent
     kernel: its (max, index) equal the fused tail's bit for bit, meet the
