@@ -112,6 +112,10 @@ template <int NTHREADS>
 __device__ void finalize_argmax(const ArgmaxWs& ws, int n_rows, float* __restrict__ out_max,
                                 int32_t* __restrict__ out_idx, unsigned long long* red) {
     const int t = threadIdx.x;
+    // every arrival of this launch has been counted: the counters can be
+    // cleared now, their stores in flight beside the key exchanges below
+    if (t <= kArriveGroups)
+        __hip_atomic_store(&ws.counters[t * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int r0 = 0; r0 < n_rows; r0 += NTHREADS) {
         const int nr = min(NTHREADS, n_rows - r0);
         red[t] = 0;
@@ -144,8 +148,6 @@ __device__ void finalize_argmax(const ArgmaxWs& ws, int n_rows, float* __restric
         }
         __syncthreads();
     }
-    if (t <= kArriveGroups)
-        __hip_atomic_store(&ws.counters[t * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Host-side view of a workspace for n_rows output rows.
