@@ -112,7 +112,7 @@ size_t topk_workspace_bytes(int64_t n_rows, int64_t V, int64_t k);
 hipError_t launch_lmhead_topk(const LmheadArgs& a, int k, float* out_val, int32_t* out_idx, int cus,
                               hipStream_t stream);
 
-// the fused one-row draft tail (lmhead_stream.hip): M == 1, H <= 6144
+// the fused one-row draft tail (lmhead_stream.hip): M == 1, H <= 8192
 bool use_draft_tail1(int64_t M, int64_t H);
 int64_t draft_tail1_grid(int64_t V);   // workgroups of the fused one-row launch
 hipError_t launch_draft_tail1(const uint16_t* hidden, const uint16_t* residual, const float* gamma, float eps,
