@@ -313,6 +313,22 @@ def test_kouter_kernel_full_width():
     check_lmhead(codes, scales, d, m, i, rows=np.array([0, 17, 40, 63]))
 
 
+# the DeepSeek-V3 shape of the LM head (H = 7168, V = 129280) through every
+# decode-regime family the dispatcher picks for it: the one-row tail on the
+# full vocab (505 workgroups, more than the one-row workspace's key slots),
+# the per-tile stream kernel, the rows kernel and the K-outer kernel's
+# eight-wave shape
+@pytest.mark.parametrize("M", [1, 5, 17, 64])
+def test_deepseek_shape_full_vocab(M):
+    H, V = 7168, 129280
+    d = inputs.random_case(91 + M, M, H, V, outliers=True)
+    h, r, g, wc, ws = to_dev(d)
+    say(f"deepseek shape M={M}: {mtpd.draft_tail_plan(M, V, H)}")
+    out_h, codes, scales, m, i = mtpd.draft_tail(h, r, g, d["eps"], wc, ws)
+    check_norm_quant(d, out_h, codes, scales)
+    say("  " + str(check_lmhead(codes, scales, d, m, i)))
+
+
 def test_stream_rows_kernel_vocab_shard_shape(workloads):
     """64 rows on one GPU's 18944-row vocab shard (the decode c=64 weight's
     first 148 blocks): every row against the oracle."""
