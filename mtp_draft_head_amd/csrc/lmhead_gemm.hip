@@ -728,12 +728,29 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
 
     // promotion factors of block kb from its scale chunk
     // (thread t: weight-scale block t / BM, row t % BM)
+    // With one entry per thread (tiles of up to 256 rows) each thread reads its
+    // row's scales of four blocks as one float4 on every fourth block and keeps
+    // them in registers for the three blocks after: a row's blocks are
+    // contiguous in the chunk, and one 4-byte read per block put the 64 rows a
+    // wave reads on 8 banks.  The 320-row tile (two entries for some threads,
+    // no registers to spare) reads one scale per block.
+    float4 sa4 = make_float4(0.f, 0.f, 0.f, 0.f);
     auto factors = [&](int slot, int kb) {
         const float* chunk =
             reinterpret_cast<const float*>(smem + C::SC_OFF + ((kb / C::SC_BLOCKS) & 1) * C::SC_BYTES);
-        for (int e = t; e < 2 * BM; e += 512) {
-            const int cb = e / BM, r = e - cb * BM;
-            ftab[slot][cb][r] = chunk[r * C::SC_BLOCKS + kb % C::SC_BLOCKS] * swtab[cb][kb];
+        const int k = kb % C::SC_BLOCKS;
+        if constexpr (2 * BM <= 512) {
+            if (t < 2 * BM) {
+                const int cb = t / BM, r = t - cb * BM;
+                if ((k & 3) == 0) sa4 = *reinterpret_cast<const float4*>(&chunk[r * C::SC_BLOCKS + k]);
+                const float sa = (k & 3) == 0 ? sa4.x : (k & 3) == 1 ? sa4.y : (k & 3) == 2 ? sa4.z : sa4.w;
+                ftab[slot][cb][r] = sa * swtab[cb][kb];
+            }
+        } else {
+            for (int e = t; e < 2 * BM; e += 512) {
+                const int cb = e / BM, r = e - cb * BM;
+                ftab[slot][cb][r] = chunk[r * C::SC_BLOCKS + k] * swtab[cb][kb];
+            }
         }
     };
 
