@@ -302,7 +302,9 @@ __global__ __launch_bounds__(512) void lmhead_gemm_kernel(
 //    per eight lanes: measured 12.4 against 10.7 TB/s of L2 -> LDS for four
 //    lanes per 64-byte half, copies alone, every CU busy), chunk c of row r
 //    at position c ^ ((r >> 1) & 7).  Global loads with a wave-uniform base
-//    and 32-bit lane offsets (buffer loads measured 5% slower).
+//    and 32-bit lane offsets (buffer loads measured 5% slower); the next
+//    block's copies are spread over the current block's MFMAs, one after
+//    each from the fifth on.
 //  - MFMA lane l supplies row l % 16 and, for its 32 K bytes, 16-byte chunks
 //    l / 16 and l / 16 + 4 of that row (A and B permute K the same way, so
 //    the dot product is unchanged): each of the two fragment reads then
@@ -423,6 +425,22 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
 __device__ __forceinline__ void dma4(const void* src, void* lds) {
     __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds, 4, 0, 0);
 }
+
+// The same 16-byte copy from a wave-uniform base in SGPRs plus a 32-bit lane
+// offset, written out so that no 64-bit lane address is formed (the builtin
+// compiled to two 64-bit vector adds per copy inside the K loop).  M0 carries
+// the LDS address (one wait state before the copy reads it).  The compiler
+// neither sees nor waits for these copies: the kernel drains them itself
+// (vmcnt(0) before each block's barrier).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 is reserved; nothing else in the loop uses it
+__device__ __forceinline__ void dma16_s(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // The same copy through a raw buffer resource of a given size: lanes whose
 // byte offset lies past the end read zeros instead of faulting.  Third
@@ -600,6 +618,29 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16(wb + woff[i], smem + C::W_OFF + s * C::W_BYTES + (4 * wave + i) * 1024);
     };
+    // Copy c (0 .. NCOPY - 1) of block kb into stage s: activation copies
+    // first, then the four weight copies; the same copies as copy_in.
+    constexpr int NCOPY = AC + 4;
+    // The next block's copies go out one per MFMA, from the block's fifth
+    // MFMA on: issued all at once at the block start they stalled every wave
+    // at issue (the address unit takes a 1 KB copy per 16 clocks) before its
+    // first fragment reads, and spread further apart they land too late
+    // (measured on compute_stress: 6.9-7.1 ms at the block start, 6.5-6.6 ms
+    // from the fifth MFMA, 6.7 ms at every second MFMA).
+    constexpr int kCopyStart = 4;
+    static_assert(kCopyStart + NCOPY <= 4 * MT, "every copy is issued inside the block");
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
+    auto copy_one = [&](int s, int kb, int c) {
+        if (c < AC) {
+            const int j = wave + 8 * c;
+            if (j < C::A_COPIES)
+                dma16_s(a_codes + (size_t)kb * kBlock, aoff[c], smem_lds + (uint32_t)(s * C::A_BYTES + j * 1024));
+        } else {
+            const int i = c - AC;
+            dma16_s(wbase + (size_t)kb * kBlock, woff[i],
+                    smem_lds + (uint32_t)(C::W_OFF + s * C::W_BYTES + (4 * wave + i) * 1024));
+        }
+    };
     // activation scales of K blocks c * SC_BLOCKS .. + SC_BLOCKS - 1 into chunk slot c % 2
     auto copy_scales = [&](int c) {
         if (wave < C::SCOPY)
@@ -654,7 +695,7 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
     // first MFMA and the fold-in of group g - 1's last one (which frees the
     // factor slot); the block's first batch is group 0's and all four weight
     // fragments, and group 0's MFMAs start as their own operands arrive.
-    auto compute = [&](int s) {
+    auto compute = [&](int s, auto&& after) {
         u32x4_t alo[2], ahi[2];
         alo[0] = lds_read16_sk<C::A_BYTES, 2048>(a_lo, s, 0);
         ahi[0] = lds_read16_sk<C::A_BYTES, 2048>(a_hi, s, 0);
@@ -670,6 +711,8 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
         bf[0] = frag_of(b0, b1);
         sched_fence();
         ring[0] = mfma_e4m3(af0, bf[0]);
+        sched_fence();
+        after(0);
         if (MT > 1) {
             alo[1] = lds_read16_sk<C::A_BYTES, 2048>(a_lo, s, 1);
             ahi[1] = lds_read16_sk<C::A_BYTES, 2048>(a_hi, s, 1);
@@ -681,6 +724,8 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
         lds_wait<NXT + 4>(b2, b3);
         bf[1] = frag_of(b2, b3);
         ring[1] = mfma_e4m3(af0, bf[1]);
+        sched_fence();
+        after(1);
         sched_fence();   // the MFMA issues first, then the previous one's fold-in
         promote(0, 0, ring[0], fv[0]);
         sched_fence();
@@ -688,11 +733,15 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
         bf[2] = frag_of(b4, b5);
         ring[0] = mfma_e4m3(af0, bf[2]);
         sched_fence();
+        after(2);
+        sched_fence();
         promote(0, 1, ring[1], fv[0]);
         sched_fence();
         lds_wait<NXT>(b6, b7);
         bf[3] = frag_of(b6, b7);
         ring[1] = mfma_e4m3(af0, bf[3]);
+        sched_fence();
+        after(3);
         sched_fence();
         promote(0, 2, ring[0], fv[0]);
         sched_fence();
@@ -703,6 +752,8 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
             const v8i af = frag_of(alo[slot], ahi[slot]);
             ring[0] = mfma_e4m3(af, bf[0]);
             sched_fence();
+            after(mt * 4 + 0);
+            sched_fence();
             promote(mt - 1, 3, ring[1], fv[slot ^ 1]);
             if (mt + 1 < MT) {
                 alo[slot ^ 1] = lds_read16_sk<C::A_BYTES, 2048>(a_lo, s, mt + 1);
@@ -712,13 +763,19 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
             sched_fence();
             ring[1] = mfma_e4m3(af, bf[1]);
             sched_fence();
+            after(mt * 4 + 1);
+            sched_fence();
             promote(mt, 0, ring[0], fv[slot]);
             sched_fence();
             ring[0] = mfma_e4m3(af, bf[2]);
             sched_fence();
+            after(mt * 4 + 2);
+            sched_fence();
             promote(mt, 1, ring[1], fv[slot]);
             sched_fence();
             ring[1] = mfma_e4m3(af, bf[3]);
+            sched_fence();
+            after(mt * 4 + 3);
             sched_fence();
             promote(mt, 2, ring[0], fv[slot]);
             sched_fence();
@@ -757,9 +814,10 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
     // ---- pipeline ----
     // Prologue: the weight-scale table, scale chunks 0 and 1, stage 0 = codes
     // of block 0; then block 0's factors.  Block kb computes from stage kb % 2
-    // and factor slot kb % 2, while the copy of block kb + 1 fills the other
-    // stage and every thread forms one factor of block kb + 1; the barrier
-    // ending the block publishes both.  Chunk c + 1 is copied at the start of
+    // and factor slot kb % 2, while the copy of block kb + 1 (issued from
+    // inside the block's MFMA sequence) fills the other stage and every thread
+    // forms one factor of block kb + 1; the barrier ending the block publishes
+    // both.  Chunk c + 1 is copied at the start of
     // block 8c (c >= 1): chunk c - 1, in that slot, was last read during block
     // 8c - 2.
     if (wave < 2)
@@ -772,15 +830,17 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
     drain_barrier();
     for (int kb = 0; kb < KB; kb += 2) {
         // stage 0 (kb is even: chunk boundaries fall here)
-        if (kb + 1 < KB) copy_in(1, kb + 1);
         if (kb > 0 && kb % C::SC_BLOCKS == 0 && kb + C::SC_BLOCKS < KB) copy_scales(kb / C::SC_BLOCKS + 1);
-        compute(0);
+        compute(0, [&](int n) {
+            if (n >= kCopyStart && n < kCopyStart + NCOPY && kb + 1 < KB) copy_one(1, kb + 1, n - kCopyStart);
+        });
         if (kb + 1 < KB) factors(1, kb + 1);
         drain_barrier();
         if (kb + 1 >= KB) break;
         // stage 1
-        if (kb + 2 < KB) copy_in(0, kb + 2);
-        compute(1);
+        compute(1, [&](int n) {
+            if (n >= kCopyStart && n < kCopyStart + NCOPY && kb + 2 < KB) copy_one(0, kb + 2, n - kCopyStart);
+        });
         if (kb + 2 < KB) factors(0, kb + 2);
         drain_barrier();
     }
