@@ -358,12 +358,21 @@ def measure_peaks(dev, log_fn):
     L.mtpd_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     L.mtpd_peak_mfma.restype = ctypes.c_int
     L.mtpd_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.mtpd_peak_mfma_random.restype = ctypes.c_int
+    L.mtpd_peak_mfma_random.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p]
     stream = torch.cuda.current_stream(dev)
     nbytes, grid = 4 << 30, 4096
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     sink = torch.empty(grid * 256, dtype=torch.int32, device=dev)
     mgrid, iters = 1024, 2048
     mout = torch.empty(mgrid * 256, dtype=torch.float32, device=dev)
+    # random E4M3 operand codes for the second MFMA loop, NaN codes (0x7f, 0xff) moved one step down
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260)
+    codes = torch.randint(0, 256, (mgrid * 256 * 32 * 4,), dtype=torch.int32, device=dev, generator=gen)
+    codes = torch.where((codes & 0x7F) == 0x7F, codes - 1, codes).to(torch.uint8)
+    words = codes.view(torch.int32)
 
     def best(fn, n=5):
         times = []
@@ -380,12 +389,16 @@ def measure_peaks(dev, log_fn):
     log_fn("[bench] measuring achievable peaks (HBM streaming read, FP8 MFMA loop)")
     t_read = best(lambda: L.mtpd_peak_read(buf.data_ptr(), nbytes, grid, sink.data_ptr(), stream.cuda_stream))
     t_mfma = best(lambda: L.mtpd_peak_mfma(iters, mgrid, mout.data_ptr(), stream.cuda_stream))
+    t_mfma_r = best(lambda: L.mtpd_peak_mfma_random(iters, mgrid, words.data_ptr(), mout.data_ptr(),
+                                                    stream.cuda_stream))
     flops = mgrid * 4 * iters * 8 * 65536.0
-    del buf, sink, mout
+    del buf, sink, mout, codes, words
     return {"hbm_read_GBps": round(nbytes / t_read / 1e9, 1),
             "fp8_mfma_TFLOPs": round(flops / t_mfma / 1e12, 1),
+            "fp8_mfma_random_operands_TFLOPs": round(flops / t_mfma_r / 1e12, 1),
             "how": "streaming read of 4 GiB (4096 workgroups, nt 16-byte loads); register-only loop of "
-                   "v_mfma_f32_16x16x128_f8f6f4 (1024 workgroups x 4 waves x 8 accumulations); best of 5"}
+                   "v_mfma_f32_16x16x128_f8f6f4 (1024 workgroups x 4 waves x 8 accumulations) on near-constant "
+                   "operands, and again on random E4M3 operands alternating between two sets per lane; best of 5"}
 
 
 def main() -> int:

@@ -65,6 +65,37 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __rest
     out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// The same loop on operands that look like real data: each lane loads two
+// random operand pairs (words: grid * 256 * 32 u32) and the MFMAs alternate
+// between them, so the multiplier inputs change from one instruction to the
+// next as they do in the LM-head kernels (the matrix cores draw more power on
+// such operands than on the near-constant ones above, and the clock follows).
+__global__ __launch_bounds__(256) void mfma_loop_random_kernel(int iters, const uint32_t* __restrict__ words,
+                                                               float* __restrict__ out) {
+    const uint32_t* w = words + ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 32;
+    v8i a0, b0, a1, b1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a0[i] = (int)w[i];
+        b0[i] = (int)w[8 + i];
+        a1[i] = (int)w[16 + i];
+        b1[i] = (int)w[24 + i];
+    }
+    v4f c[kChains];
+#pragma unroll
+    for (int j = 0; j < kChains; ++j) c[j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < kChains; ++j)
+            c[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(j & 1 ? a1 : a0, j & 1 ? b1 : b0, c[j], 0, 0, 0, 0,
+                                                                    0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < kChains; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -85,6 +116,15 @@ int mtpd_peak_read(const void* src, uint64_t bytes, int grid, unsigned* sink, vo
 int mtpd_peak_mfma(int iters, int grid, float* out, void* stream) {
     if (!out || grid < 1 || iters < 1) return 1;
     hipLaunchKernelGGL(mfma_loop_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// The loop on random operands: words holds grid * 256 * 32 u32 of device
+// memory (random E4M3 codes; the caller keeps NaN codes out, as the packing
+// never produces them).
+int mtpd_peak_mfma_random(int iters, int grid, const uint32_t* words, float* out, void* stream) {
+    if (!out || !words || grid < 1 || iters < 1) return 1;
+    hipLaunchKernelGGL(mfma_loop_random_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, words, out);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
