@@ -674,8 +674,7 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) opaque(acc[i][j][r]);
 
-    v4f ring[2];        // the last two MFMA results, each folded in one MFMA later
-    u32x4_t fv[2];      // promotion factors of a row group's four rows (by group parity)
+    v4f ring[3];        // the last three MFMA results, each folded in two MFMAs later
 
     // (each updated accumulator passes through an empty asm, so the FMA stays
     // where it is written: left alone, the compiler sinks every fold-in of a
@@ -688,15 +687,19 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
         }
     };
 
-    // One K block from stage s, factor slot s.  MFMA (g, nt) -> ring[n % 2]
-    // (n its index in the block); its fold-in follows the next MFMA, so the
-    // matrix result is ready by then and the other wave fills the gap.  Read
-    // order: group g + 1's activation and factors are issued after group g's
-    // first MFMA and the fold-in of group g - 1's last one (which frees the
-    // factor slot); the block's first batch is group 0's and all four weight
-    // fragments, and group 0's MFMAs start as their own operands arrive.
+    // One K block from stage s, factor slot s.  MFMA n of the block (row
+    // group n / 4, column group n % 4) goes to ring[n % 3], and its fold-in
+    // follows MFMA n + 2: by then the matrix result is ready without wait
+    // states (folding in one MFMA later needed s_nop padding before every
+    // fold-in, and measured 2% slower on both compute-regime workloads).
+    // Reads: the block's first batch is row group 0's activation fragment
+    // and factors and all four weight fragments, and group 0's MFMAs start as
+    // their own operands arrive; group g + 1's activation and factors are
+    // issued after group g's first MFMA, into the activation slot of group
+    // g - 1 (whose MFMAs have all issued) and the factor slot of group g - 2
+    // (whose fold-ins are done).
     auto compute = [&](int s, auto&& after) {
-        u32x4_t alo[2], ahi[2];
+        u32x4_t alo[2], ahi[2], fv[3];
         alo[0] = lds_read16_sk<C::A_BYTES, 2048>(a_lo, s, 0);
         ahi[0] = lds_read16_sk<C::A_BYTES, 2048>(a_hi, s, 0);
         fv[0] = lds_read16_sk<FSLOT, 64>(f_ad, s, 0);
@@ -705,82 +708,48 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
         u32x4_t b4 = lds_read16_sk<C::W_BYTES, 2048>(b_lo, s, 2), b5 = lds_read16_sk<C::W_BYTES, 2048>(b_hi, s, 2);
         u32x4_t b6 = lds_read16_sk<C::W_BYTES, 2048>(b_lo, s, 3), b7 = lds_read16_sk<C::W_BYTES, 2048>(b_hi, s, 3);
         v8i bf[4];
-        // in flight: A0 (2), F0, B0 .. B3 (8): the first 5 are group 0's and B0
-        lds_wait<6>(alo[0], ahi[0], fv[0], b0, b1);
-        const v8i af0 = frag_of(alo[0], ahi[0]);
-        bf[0] = frag_of(b0, b1);
-        sched_fence();
-        ring[0] = mfma_e4m3(af0, bf[0]);
-        sched_fence();
-        after(0);
-        if (MT > 1) {
-            alo[1] = lds_read16_sk<C::A_BYTES, 2048>(a_lo, s, 1);
-            ahi[1] = lds_read16_sk<C::A_BYTES, 2048>(a_hi, s, 1);
-            fv[1] = lds_read16_sk<FSLOT, 64>(f_ad, s, 1);
-        }
-        sched_fence();
-        // in flight: B1 .. B3 (6), then group 1's 3
+        v8i af;
+        // group 1's three reads follow group 0's first MFMA, so the waits for
+        // weight fragments 1 .. 3 leave them (and the younger weight reads) in flight
         constexpr int NXT = MT > 1 ? 3 : 0;
-        lds_wait<NXT + 4>(b2, b3);
-        bf[1] = frag_of(b2, b3);
-        ring[1] = mfma_e4m3(af0, bf[1]);
-        sched_fence();
-        after(1);
-        sched_fence();   // the MFMA issues first, then the previous one's fold-in
-        promote(0, 0, ring[0], fv[0]);
-        sched_fence();
-        lds_wait<NXT + 2>(b4, b5);
-        bf[2] = frag_of(b4, b5);
-        ring[0] = mfma_e4m3(af0, bf[2]);
-        sched_fence();
-        after(2);
-        sched_fence();
-        promote(0, 1, ring[1], fv[0]);
-        sched_fence();
-        lds_wait<NXT>(b6, b7);
-        bf[3] = frag_of(b6, b7);
-        ring[1] = mfma_e4m3(af0, bf[3]);
-        sched_fence();
-        after(3);
-        sched_fence();
-        promote(0, 2, ring[0], fv[0]);
-        sched_fence();
 #pragma unroll
-        for (int mt = 1; mt < MT; ++mt) {
-            const int slot = mt & 1;
-            lds_wait<0>(alo[slot], ahi[slot], fv[slot]);
-            const v8i af = frag_of(alo[slot], ahi[slot]);
-            ring[0] = mfma_e4m3(af, bf[0]);
-            sched_fence();
-            after(mt * 4 + 0);
-            sched_fence();
-            promote(mt - 1, 3, ring[1], fv[slot ^ 1]);
-            if (mt + 1 < MT) {
-                alo[slot ^ 1] = lds_read16_sk<C::A_BYTES, 2048>(a_lo, s, mt + 1);
-                ahi[slot ^ 1] = lds_read16_sk<C::A_BYTES, 2048>(a_hi, s, mt + 1);
-                fv[slot ^ 1] = lds_read16_sk<FSLOT, 64>(f_ad, s, mt + 1);
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int n = mt * 4 + nt;
+                if (n == 0) {
+                    // in flight: A0 (2), F0, B0 .. B3 (8): the first 5 are group 0's and B0
+                    lds_wait<6>(alo[0], ahi[0], fv[0], b0, b1);
+                    af = frag_of(alo[0], ahi[0]);
+                    bf[0] = frag_of(b0, b1);
+                } else if (n == 1) {
+                    lds_wait<NXT + 4>(b2, b3);
+                    bf[1] = frag_of(b2, b3);
+                } else if (n == 2) {
+                    lds_wait<NXT + 2>(b4, b5);
+                    bf[2] = frag_of(b4, b5);
+                } else if (n == 3) {
+                    lds_wait<NXT>(b6, b7);
+                    bf[3] = frag_of(b6, b7);
+                } else if (nt == 0) {
+                    lds_wait<0>(alo[mt & 1], ahi[mt & 1], fv[mt % 3]);
+                    af = frag_of(alo[mt & 1], ahi[mt & 1]);
+                }
+                sched_fence();
+                ring[n % 3] = mfma_e4m3(af, bf[nt]);
+                sched_fence();
+                after(n);
+                sched_fence();   // the MFMA issues first, then an older one's fold-in
+                if (n >= 2) promote((n - 2) >> 2, (n - 2) & 3, ring[(n - 2) % 3], fv[((n - 2) >> 2) % 3]);
+                if (nt == 0 && mt + 1 < MT) {
+                    alo[(mt + 1) & 1] = lds_read16_sk<C::A_BYTES, 2048>(a_lo, s, mt + 1);
+                    ahi[(mt + 1) & 1] = lds_read16_sk<C::A_BYTES, 2048>(a_hi, s, mt + 1);
+                    fv[(mt + 1) % 3] = lds_read16_sk<FSLOT, 64>(f_ad, s, mt + 1);
+                }
+                sched_fence();
             }
-            sched_fence();
-            ring[1] = mfma_e4m3(af, bf[1]);
-            sched_fence();
-            after(mt * 4 + 1);
-            sched_fence();
-            promote(mt, 0, ring[0], fv[slot]);
-            sched_fence();
-            ring[0] = mfma_e4m3(af, bf[2]);
-            sched_fence();
-            after(mt * 4 + 2);
-            sched_fence();
-            promote(mt, 1, ring[1], fv[slot]);
-            sched_fence();
-            ring[1] = mfma_e4m3(af, bf[3]);
-            sched_fence();
-            after(mt * 4 + 3);
-            sched_fence();
-            promote(mt, 2, ring[0], fv[slot]);
-            sched_fence();
-        }
-        promote(MT - 1, 3, ring[1], fv[(MT - 1) & 1]);
+#pragma unroll
+        for (int n = 4 * MT - 2; n < 4 * MT; ++n) promote(n >> 2, n & 3, ring[n % 3], fv[(n >> 2) % 3]);
     };
 
     // promotion factors of block kb from its scale chunk
