@@ -310,12 +310,23 @@ __global__ __launch_bounds__(512) void lmhead_gemm_kernel(
 //    the dot product is unchanged): each of the two fragment reads then
 //    touches 16 rows at one chunk each, and the swizzle spreads any 16
 //    consecutive lanes over all 64 banks.
+//  - Operand order: each MFMA takes the weight fragment first, so a lane's
+//    four results of one MFMA are four vocab columns of one activation row.
+//    They share one promotion factor, and the row's argmax is mostly in-lane
+//    work: 16 values per lane and row group, then two cross-lane steps
+//    (about 470 VALU instructions per wave for the epilogue, against about
+//    860 with the activation fragment first; the FMAs and matrix
+//    instructions together fill about 90% of the SIMD cycles, so every VALU
+//    instruction costs time).  Measured on compute_stress in one call:
+//    6.14 against 6.25 ms; mtp5_batch unchanged.
 //  - Block scales: the activation scales arrive eight K blocks at a time
 //    (32 bytes per row, two lanes per row: one request per eight rows'
 //    lines instead of one per row per block, which cost 15% of the copy
 //    rate); during block kb every thread forms one entry sa[row] * sw[block]
 //    of block kb + 1's factor table (2 weight-scale blocks x BM rows), so
 //    the promotion reads its factors instead of multiplying them per wave.
+//    The table is in lane order, so a lane reads its MT factors of a block
+//    in MT / 4 16-byte reads and one 8- or 4-byte read.
 //  - Per K block a wave issues its first row group's activation fragment and
 //    factors and its four weight fragments, then starts each of the first
 //    group's MFMAs as soon as that MFMA's own operands have arrived (reads
@@ -377,6 +388,46 @@ __device__ __forceinline__ u32x4_t lds_read16_sk(uint32_t addr, int s, int k) {
 #undef MTPD_CASE
 }
 
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+template <int OFF>
+__device__ __forceinline__ u32x2_t lds_read8_off(uint32_t addr) {
+    u32x2_t v;
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t lds_read4_off(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+
+// The factor reads of stage s (0, 1): a full chunk c (0..2) of four row
+// groups' factors, 16 bytes per lane; the partial chunk (one or two row
+// groups) at stage offset only.  s and c are known after unrolling.
+template <int SBYTES>
+__device__ __forceinline__ u32x4_t lds_read_fchunk(uint32_t addr, int s, int c) {
+    static_assert(SBYTES + 2 * 256 < 65536, "immediate offset range");
+    switch (s * 4 + c) {
+        case 0: return lds_read16_off<0>(addr);
+        case 1: return lds_read16_off<256>(addr);
+        case 2: return lds_read16_off<512>(addr);
+        case 4: return lds_read16_off<SBYTES>(addr);
+        case 5: return lds_read16_off<SBYTES + 256>(addr);
+        case 6: return lds_read16_off<SBYTES + 512>(addr);
+        default: __builtin_unreachable();
+    }
+}
+template <int SBYTES>
+__device__ __forceinline__ u32x2_t lds_read_fpart2(uint32_t addr, int s) {
+    return s == 0 ? lds_read8_off<0>(addr) : lds_read8_off<SBYTES>(addr);
+}
+template <int SBYTES>
+__device__ __forceinline__ uint32_t lds_read_fpart1(uint32_t addr, int s) {
+    return s == 0 ? lds_read4_off<0>(addr) : lds_read4_off<SBYTES>(addr);
+}
+
 __device__ __forceinline__ v8i frag_of(u32x4_t lo, u32x4_t hi) {
     v8i f;
     f[0] = (int)lo[0]; f[1] = (int)lo[1]; f[2] = (int)lo[2]; f[3] = (int)lo[3];
@@ -398,8 +449,20 @@ __device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b, u32x4_t& c) {
     asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(a), "+v"(b), "+v"(c) : "n"(N));
 }
 template <int N>
+__device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b, u32x4_t& c, u32x4_t& d) {
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
+}
+template <int N>
 __device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b, u32x4_t& c, u32x4_t& d, u32x4_t& e) {
     asm volatile("s_waitcnt lgkmcnt(%5)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b, u32x2_t& c) {
+    asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(a), "+v"(b), "+v"(c) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b, uint32_t& c) {
+    asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(a), "+v"(b), "+v"(c) : "n"(N));
 }
 
 // 1 if the predicate holds on any lane of the wave
@@ -457,18 +520,6 @@ __device__ __forceinline__ void bdma16(rsrc_t r, uint32_t voff, uint32_t soff, v
 // hides a value from constant folding (the zero accumulators of the first block)
 __device__ __forceinline__ void opaque(float& x) { asm volatile("" : "+v"(x)); }
 
-// Row reductions of the epilogue.  The code around them has no branches, so
-// every lane runs every move and a move never reads a disabled lane; the moves
-// are left unpinned so that the compiler folds each into its max or min, and
-// the reductions run breadth first over eight (or four) rows at a time, so
-// that no move waits on the value written just before it.  Controls as for row16_max:
-// lane ^ 1, lane ^ 2, the half-row mirror and the row mirror, all inside a
-// 16-lane row.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_row_u32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
-}
-
 // the order-preserving u32 of a logit (argmax_key's upper word; -0 folds onto
 // +0 through the addition)
 __device__ __forceinline__ uint32_t ord_f32(float z) {
@@ -476,61 +527,38 @@ __device__ __forceinline__ uint32_t ord_f32(float z) {
     return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
-// Per-row best of a wave's 16 x 64 sub-tiles, written to LDS: for row group
-// mt and lane row i (row mt * 16 + 4 * (lane / 16) + i), the argmax key of
-// the largest value and the lowest column holding it (columns col0 + lane % 16
-// + 16 nt) goes to dst[mt * 16 + 4 * (lane / 16) + i].  Each lane first finds
-// its largest value and the lowest of its four columns holding it; the row's
-// maximum over the 16 lanes follows as an ordered u32, and the lowest column
-// among the lanes whose maximum equals it.  fp32 compares (and the ordered
-// u32, which folds -0 onto +0) treat -0 and +0 as equal, as the key does.
+// Per-row best of a wave's 16 x 64 sub-tiles, written to LDS.  The MFMAs
+// take the weight fragment as their first operand, so lane l holds, for row
+// group mt, the 16 values of activation row mt * 16 + l % 16 at columns
+// col0 + 16 nt + 4 (l / 16) + r (nt, r = 0..3).  Each lane takes its largest
+// value and the lowest of its columns holding it; the four lanes sharing a
+// row (l, l + 16, l + 32, l + 48) then agree on the row's maximum and the
+// lowest column among the lanes that hold it, and lane l < 16 writes the key
+// to dst[mt * 16 + l].  fp32 compares treat -0 and +0 as equal, as the key
+// does (ord_f32 folds -0 onto +0).
 template <int MT>
 __device__ __forceinline__ void row_best_keys(const float (&acc)[MT][4][4], int lane, uint32_t col0,
                                               unsigned long long* dst) {
-    constexpr int B = MT % 2 == 0 ? 8 : 4;
-    const uint32_t l16 = (uint32_t)(lane & 15);
+    const uint32_t q4 = (uint32_t)(lane >> 4) * 4u;
 #pragma unroll
-    for (int p0 = 0; p0 < MT * 4; p0 += B) {
-        constexpr int N = B;
-        uint32_t o[N], om[N], c[N];
+    for (int mt = 0; mt < MT; ++mt) {
+        float m = acc[mt][0][0];
 #pragma unroll
-        for (int q = 0; q < N; ++q) {
-            const int mt = (p0 + q) >> 2, i = (p0 + q) & 3;
-            const float v0 = acc[mt][0][i], v1 = acc[mt][1][i], v2 = acc[mt][2][i], v3 = acc[mt][3][i];
-            const float m = fmaxf(fmaxf(v0, v1), fmaxf(v2, v3));
-            uint32_t cc = l16 + 48u;
-            cc = v2 == m ? l16 + 32u : cc;
-            cc = v1 == m ? l16 + 16u : cc;
-            cc = v0 == m ? l16 : cc;
-            c[q] = cc;
-            o[q] = ord_f32(m);
-            om[q] = o[q];
-        }
+        for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int q = 0; q < N; ++q) om[q] = max(om[q], dpp_row_u32<0xB1>(om[q]));
+            for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[mt][nt][r]);
+        uint32_t c = 0xFFFFu;
 #pragma unroll
-        for (int q = 0; q < N; ++q) om[q] = max(om[q], dpp_row_u32<0x4E>(om[q]));
+        for (int nt = 3; nt >= 0; --nt)
 #pragma unroll
-        for (int q = 0; q < N; ++q) om[q] = max(om[q], dpp_row_u32<0x141>(om[q]));
-#pragma unroll
-        for (int q = 0; q < N; ++q) om[q] = max(om[q], dpp_row_u32<0x140>(om[q]));
-#pragma unroll
-        for (int q = 0; q < N; ++q) c[q] = o[q] == om[q] ? c[q] : 0x10000u;
-#pragma unroll
-        for (int q = 0; q < N; ++q) c[q] = min(c[q], dpp_row_u32<0xB1>(c[q]));
-#pragma unroll
-        for (int q = 0; q < N; ++q) c[q] = min(c[q], dpp_row_u32<0x4E>(c[q]));
-#pragma unroll
-        for (int q = 0; q < N; ++q) c[q] = min(c[q], dpp_row_u32<0x141>(c[q]));
-#pragma unroll
-        for (int q = 0; q < N; ++q) c[q] = min(c[q], dpp_row_u32<0x140>(c[q]));
-        if ((lane & 15) == 0) {
-#pragma unroll
-            for (int q = 0; q < N; ++q) {
-                const int mt = (p0 + q) >> 2, i = (p0 + q) & 3;
-                dst[mt * 16 + 4 * (lane >> 4) + i] = ((uint64_t)om[q] << 32) | (uint64_t)(0xFFFFFFFFu - (col0 + c[q]));
-            }
-        }
+            for (int r = 3; r >= 0; --r) c = acc[mt][nt][r] == m ? (uint32_t)(nt * 16 + r) : c;
+        c += q4;
+        float mx = fmaxf(m, __shfl_xor(m, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        uint32_t cc = m == mx ? c : 0xFFFFu;
+        cc = min(cc, (uint32_t)__shfl_xor((int)cc, 16));
+        cc = min(cc, (uint32_t)__shfl_xor((int)cc, 32));
+        if (lane < 16) dst[mt * 16 + lane] = ((uint64_t)ord_f32(mx) << 32) | (uint64_t)(0xFFFFFFFFu - (col0 + cc));
     }
 }
 
@@ -549,7 +577,15 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
     static_assert(C::SMEM + 2 * 2 * BM * 4 + 2 * C::SW_MAX * 4 <= 160 * 1024, "LDS");
     static_assert(4 * BM * 8 <= C::SMEM, "epilogue table must fit in the stage memory");
     __shared__ __align__(16) unsigned char smem[C::SMEM];
-    __shared__ __align__(16) float ftab[2][2][BM];        // [slot][weight-scale block][row] promotion factors
+    // promotion factors sa[row] * sw[block] of two K blocks (slots): per slot,
+    // weight-scale block cb and row half wm, the 16 * MT factors of that half
+    // in lane order: chunk c (row groups 4c .. 4c + 3) holds lane row j's four
+    // at 16 j, the partial chunk (the last MT % 4 groups) its MT % 4 at
+    // FP * 4 j, so a lane reads its factors for a block in MT / 4 16-byte reads
+    // and one 8- or 4-byte read
+    constexpr int FC = MT / 4, FP = MT % 4;
+    static_assert(FC >= 1 && FC <= 3 && FP != 3, "factor chunks");
+    __shared__ __align__(16) float ftab[2 * 2 * 2 * 16 * MT];
     __shared__ __align__(16) float swtab[2][C::SW_MAX];   // weight scales of the tile's two 128-row blocks
     __shared__ unsigned int deps[8];
     __shared__ int last_flag;
@@ -657,8 +693,10 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
     const uint32_t a_hi = smem0 + (uint32_t)(wm * MT * 16 * 128) + hi16;
     const uint32_t b_lo = smem0 + (uint32_t)(C::W_OFF + wn * 64 * 128) + lo16;
     const uint32_t b_hi = smem0 + (uint32_t)(C::W_OFF + wn * 64 * 128) + hi16;
-    const uint32_t f_ad = (uint32_t)(uintptr_t)(lds_ptr_t)&ftab[0][wn >> 1][wm * MT * 16 + 4 * fg];
-    constexpr int FSLOT = 2 * BM * 4;   // bytes between the two factor slots
+    constexpr int FSLOT = 2 * 2 * 16 * MT * 4;   // bytes between the two factor slots
+    const uint32_t f_reg = (uint32_t)(uintptr_t)(lds_ptr_t)&ftab[((wn >> 1) * 2 + wm) * 16 * MT];
+    const uint32_t f_full = f_reg + (uint32_t)(fr * 16);
+    const uint32_t f_part = f_reg + (uint32_t)(FC * 256 + fr * FP * 4);
 
     float acc[MT][4][4];
 #pragma unroll
@@ -678,78 +716,96 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
 
     // (each updated accumulator passes through an empty asm, so the FMA stays
     // where it is written: left alone, the compiler sinks every fold-in of a
-    // block past the block's barrier, keeping all its MFMA results live)
-    auto promote = [&](int mt, int nt, const v4f& p, const u32x4_t& f) {
+    // block past the block's barrier, keeping all its MFMA results live).
+    // The four values of a lane in one MFMA result share the lane's
+    // activation row, so they share one factor.
+    auto promote = [&](int mt, int nt, const v4f& p, uint32_t f) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            acc[mt][nt][r] = fmaf(p[r], __uint_as_float(f[r]), acc[mt][nt][r]);
+            acc[mt][nt][r] = fmaf(p[r], __uint_as_float(f), acc[mt][nt][r]);
             opaque(acc[mt][nt][r]);
         }
     };
 
     // One K block from stage s, factor slot s.  MFMA n of the block (row
-    // group n / 4, column group n % 4) goes to ring[n % 3], and its fold-in
-    // follows MFMA n + 2: by then the matrix result is ready without wait
-    // states (folding in one MFMA later needed s_nop padding before every
-    // fold-in, and measured 2% slower on both compute-regime workloads).
-    // Reads: the block's first batch is row group 0's activation fragment
-    // and factors and all four weight fragments, and group 0's MFMAs start as
-    // their own operands arrive; group g + 1's activation and factors are
-    // issued after group g's first MFMA, into the activation slot of group
-    // g - 1 (whose MFMAs have all issued) and the factor slot of group g - 2
-    // (whose fold-ins are done).
+    // group n / 4, column group n % 4) takes the weight fragment as its first
+    // operand and goes to ring[n % 3]; its fold-in follows MFMA n + 2: by then
+    // the matrix result is ready without wait states (folding in one MFMA
+    // later needed s_nop padding before every fold-in, and measured 2% slower
+    // on both compute-regime workloads).
+    // Reads: the block's first batch is row group 0's activation fragment, all
+    // four weight fragments and the factors of row groups 0 .. 3 (after the
+    // second weight fragment: the first fold-in follows the third MFMA), and
+    // group 0's MFMAs start as their own operands arrive; group g + 1's
+    // activation fragment (and, when g + 1 starts a chunk, that chunk of
+    // factors) is issued after group g's first MFMA, into the activation slot
+    // of group g - 1, whose MFMAs have all issued.
     auto compute = [&](int s, auto&& after) {
-        u32x4_t alo[2], ahi[2], fv[3];
+        u32x4_t alo[2], ahi[2], fc[FC];
+        u32x2_t fp2 = {0u, 0u};
+        uint32_t fp1 = 0u;
         alo[0] = lds_read16_sk<C::A_BYTES, 2048>(a_lo, s, 0);
         ahi[0] = lds_read16_sk<C::A_BYTES, 2048>(a_hi, s, 0);
-        fv[0] = lds_read16_sk<FSLOT, 64>(f_ad, s, 0);
         u32x4_t b0 = lds_read16_sk<C::W_BYTES, 2048>(b_lo, s, 0), b1 = lds_read16_sk<C::W_BYTES, 2048>(b_hi, s, 0);
         u32x4_t b2 = lds_read16_sk<C::W_BYTES, 2048>(b_lo, s, 1), b3 = lds_read16_sk<C::W_BYTES, 2048>(b_hi, s, 1);
+        fc[0] = lds_read_fchunk<FSLOT>(f_full, s, 0);
         u32x4_t b4 = lds_read16_sk<C::W_BYTES, 2048>(b_lo, s, 2), b5 = lds_read16_sk<C::W_BYTES, 2048>(b_hi, s, 2);
         u32x4_t b6 = lds_read16_sk<C::W_BYTES, 2048>(b_lo, s, 3), b7 = lds_read16_sk<C::W_BYTES, 2048>(b_hi, s, 3);
         v8i bf[4];
         v8i af;
-        // group 1's three reads follow group 0's first MFMA, so the waits for
-        // weight fragments 1 .. 3 leave them (and the younger weight reads) in flight
-        constexpr int NXT = MT > 1 ? 3 : 0;
+        auto factor = [&](int mt) -> uint32_t {
+            if (mt < 4 * FC) return fc[mt >> 2][mt & 3];
+            if constexpr (FP == 2) return fp2[mt - 4 * FC];
+            return fp1;
+        };
+        // group 1's two reads follow group 0's first MFMA, so the waits for
+        // weight fragments 1 .. 3 leave them (and the younger reads) in flight
+        constexpr int NXT = MT > 1 ? 2 : 0;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 const int n = mt * 4 + nt;
                 if (n == 0) {
-                    // in flight: A0 (2), F0, B0 .. B3 (8): the first 5 are group 0's and B0
-                    lds_wait<6>(alo[0], ahi[0], fv[0], b0, b1);
+                    // in flight: A0 (2), B0, B1 (4), F0, B2, B3 (4): the first 4 are group 0's and B0
+                    lds_wait<7>(alo[0], ahi[0], b0, b1);
                     af = frag_of(alo[0], ahi[0]);
                     bf[0] = frag_of(b0, b1);
                 } else if (n == 1) {
-                    lds_wait<NXT + 4>(b2, b3);
+                    lds_wait<NXT + 5>(b2, b3);
                     bf[1] = frag_of(b2, b3);
                 } else if (n == 2) {
-                    lds_wait<NXT + 2>(b4, b5);
+                    lds_wait<NXT + 2>(b4, b5, fc[0]);
                     bf[2] = frag_of(b4, b5);
                 } else if (n == 3) {
                     lds_wait<NXT>(b6, b7);
                     bf[3] = frag_of(b6, b7);
                 } else if (nt == 0) {
-                    lds_wait<0>(alo[mt & 1], ahi[mt & 1], fv[mt % 3]);
+                    if (mt % 4 == 0 && mt < 4 * FC) lds_wait<0>(alo[mt & 1], ahi[mt & 1], fc[mt >> 2]);
+                    else if (mt == 4 * FC && FP == 2) lds_wait<0>(alo[mt & 1], ahi[mt & 1], fp2);
+                    else if (mt == 4 * FC && FP == 1) lds_wait<0>(alo[mt & 1], ahi[mt & 1], fp1);
+                    else lds_wait<0>(alo[mt & 1], ahi[mt & 1]);
                     af = frag_of(alo[mt & 1], ahi[mt & 1]);
                 }
                 sched_fence();
-                ring[n % 3] = mfma_e4m3(af, bf[nt]);
+                ring[n % 3] = mfma_e4m3(bf[nt], af);
                 sched_fence();
                 after(n);
                 sched_fence();   // the MFMA issues first, then an older one's fold-in
-                if (n >= 2) promote((n - 2) >> 2, (n - 2) & 3, ring[(n - 2) % 3], fv[((n - 2) >> 2) % 3]);
+                if (n >= 2) promote((n - 2) >> 2, (n - 2) & 3, ring[(n - 2) % 3], factor((n - 2) >> 2));
                 if (nt == 0 && mt + 1 < MT) {
                     alo[(mt + 1) & 1] = lds_read16_sk<C::A_BYTES, 2048>(a_lo, s, mt + 1);
                     ahi[(mt + 1) & 1] = lds_read16_sk<C::A_BYTES, 2048>(a_hi, s, mt + 1);
-                    fv[(mt + 1) % 3] = lds_read16_sk<FSLOT, 64>(f_ad, s, mt + 1);
+                    if ((mt + 1) % 4 == 0 && mt + 1 < 4 * FC) fc[(mt + 1) >> 2] = lds_read_fchunk<FSLOT>(f_full, s, (mt + 1) >> 2);
+                    if (mt + 1 == 4 * FC) {
+                        if constexpr (FP == 2) fp2 = lds_read_fpart2<FSLOT>(f_part, s);
+                        if constexpr (FP == 1) fp1 = lds_read_fpart1<FSLOT>(f_part, s);
+                    }
                 }
                 sched_fence();
             }
 #pragma unroll
-        for (int n = 4 * MT - 2; n < 4 * MT; ++n) promote(n >> 2, n & 3, ring[n % 3], fv[(n >> 2) % 3]);
+        for (int n = 4 * MT - 2; n < 4 * MT; ++n) promote(n >> 2, n & 3, ring[n % 3], factor(n >> 2));
     };
 
     // promotion factors of block kb from its scale chunk
@@ -761,6 +817,14 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
     // wave reads on 8 banks.  The 320-row tile (two entries for some threads,
     // no registers to spare) reads one scale per block.
     float4 sa4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    // position in slot 0 of the factor of weight-scale block cb and tile row r
+    auto fpos = [](int cb, int r) {
+        const int wm_ = r / (16 * MT), rem = r - wm_ * 16 * MT, mt = rem >> 4, j = rem & 15;
+        const int in = mt < 4 * FC ? 64 * (mt >> 2) + 4 * j + (mt & 3) : 64 * FC + FP * j + (mt - 4 * FC);
+        return (cb * 2 + wm_) * 16 * MT + in;
+    };
+    constexpr int FSLOTF = FSLOT / 4;
+    const int fpos_t = t < 2 * BM ? fpos(t / BM, t % BM) : 0;
     auto factors = [&](int slot, int kb) {
         const float* chunk =
             reinterpret_cast<const float*>(smem + C::SC_OFF + ((kb / C::SC_BLOCKS) & 1) * C::SC_BYTES);
@@ -770,12 +834,12 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
                 const int cb = t / BM, r = t - cb * BM;
                 if ((k & 3) == 0) sa4 = *reinterpret_cast<const float4*>(&chunk[r * C::SC_BLOCKS + k]);
                 const float sa = (k & 3) == 0 ? sa4.x : (k & 3) == 1 ? sa4.y : (k & 3) == 2 ? sa4.z : sa4.w;
-                ftab[slot][cb][r] = sa * swtab[cb][kb];
+                ftab[slot * FSLOTF + fpos_t] = sa * swtab[cb][kb];
             }
         } else {
             for (int e = t; e < 2 * BM; e += 512) {
                 const int cb = e / BM, r = e - cb * BM;
-                ftab[slot][cb][r] = chunk[r * C::SC_BLOCKS + k] * swtab[cb][kb];
+                ftab[slot * FSLOTF + fpos(cb, r)] = chunk[r * C::SC_BLOCKS + k] * swtab[cb][kb];
             }
         }
     };
