@@ -401,6 +401,59 @@ def measure_peaks(dev, log_fn):
                    "operands, and again on random E4M3 operands alternating between two sets per lane; best of 5"}
 
 
+NQ_SHAPES = [(1, 6144), (8, 6144), (64, 6144), (320, 7168), (1024, 6144), (8192, 6144)]
+
+
+def norm_quant_shapes(steps: int) -> int:
+    """norm_quant in its two launch shapes, a workgroup per row (the library's)
+    and a wavefront per row (plan override norm_quant=wave), at the decode,
+    batched-drafting and compute-stress row counts: per shape, `steps`
+    launches captured in one HIP graph and timed with HIP events, each kind
+    twice, interleaved.  Prints one JSON line per shape (microseconds per
+    launch and GB/s of the algorithmic bytes 7H + H/32 per row)."""
+    import torch
+
+    import mtp_draft_head_amd as mtpd
+
+    dev = "cuda:0"
+    for M, H in NQ_SHAPES:
+        g = torch.Generator(device=dev).manual_seed(M)
+        n = max(1, min(8, (256 << 20) // (M * H * 4)))   # input copies rotated past the Infinity Cache
+        hs = [torch.randn(M, H, device=dev, generator=g).to(torch.bfloat16) for _ in range(n)]
+        rs = [torch.randn(M, H, device=dev, generator=g).to(torch.bfloat16) for _ in range(n)]
+        w = torch.rand(H, device=dev, generator=g) + 0.5
+        out = (torch.empty(M, H, dtype=torch.bfloat16, device=dev), torch.empty(M, H, dtype=torch.uint8, device=dev),
+               torch.empty(M, H // 128, dtype=torch.float32, device=dev))
+        row = {"M": M, "H": H}
+        for kind in ["workgroup", "wave", "workgroup", "wave"]:
+            with mtpd.plan_override(norm_quant=kind):
+                plan = mtpd.draft_tail_plan(max(M, 2), 256, H).split(" + ")[0]
+                for i in range(3):
+                    mtpd.norm_quant(hs[i % n], rs[i % n], w, 1e-6, out=out)
+                torch.cuda.synchronize()
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=s):
+                    for i in range(steps):
+                        mtpd.norm_quant(hs[i % n], rs[i % n], w, 1e-6, out=out)
+                torch.cuda.synchronize()
+                graph.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(s)
+                with torch.cuda.stream(s):
+                    graph.replay()
+                e1.record(s)
+                torch.cuda.synchronize()
+                row.setdefault(kind, {"kernel": plan, "us": []})["us"].append(round(e0.elapsed_time(e1) * 1e3 / steps, 2))
+        nbytes = 7 * M * H + M * H // 32
+        for kind in ("workgroup", "wave"):
+            row[kind]["GB/s"] = round(nbytes / min(row[kind]["us"]) / 1e3, 1)
+        print(json.dumps(row), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -422,6 +475,9 @@ def main() -> int:
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_CSV", "BENCH_LOG"),
                     help="turn a rocprofv3 --pmc CSV of the MFMA counters and a bench log of the same workload "
                          "into the matrix-core utilisation summary under profiles/")
+    ap.add_argument("--norm-quant-shapes", action="store_true",
+                    help="time norm_quant as a workgroup per row and as a wavefront per row at six row counts "
+                         "(one JSON line per shape) instead of the step")
     args = ap.parse_args()
     global TOPK_K
     TOPK_K = args.topk
@@ -434,6 +490,9 @@ def main() -> int:
         print("bench.py drives exactly one GPU: the multi-GPU path (vocab shards combined by a u64 max "
               "all-reduce) is design-only in this build; run with --gpus 1", file=sys.stderr)
         return 2
+
+    if args.norm_quant_shapes:
+        return norm_quant_shapes(min(args.steps, 50))
 
     import numpy as np
     import torch

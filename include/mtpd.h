@@ -295,6 +295,8 @@ const char *mtpd_draft_tail_plan(int64_t M, int64_t V, int64_t H);
  *   "lmhead_kouter"   "0" (never) or "nt,nw,d,tmax" (only that shape)
  *   "lmhead_gemm"     "n"            compute-regime kernel variant (0 automatic)
  *   "draft_tail"      "split" (one row runs as two launches, not fused)
+ *   "norm_quant"      "wave" (a wavefront per row, H <= 8192) or
+ *                     "workgroup" (a workgroup per row, the default)
  *   "device_cus"      "n"            size persistent grids for n CUs
  *
  * A NULL value clears that key; a NULL key clears every key.  Returns

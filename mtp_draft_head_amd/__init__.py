@@ -208,7 +208,7 @@ def _stream(device: torch.device) -> int:
 
 
 _OVERRIDE_KEYS = ("lmhead_kernel", "lmhead_tile", "lmhead_stream", "lmhead_rows", "lmhead_decode",
-                  "lmhead_kouter", "lmhead_gemm", "draft_tail", "device_cus")
+                  "lmhead_kouter", "lmhead_gemm", "draft_tail", "device_cus", "norm_quant")
 
 
 class plan_override:

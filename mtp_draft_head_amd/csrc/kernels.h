@@ -102,6 +102,7 @@ struct PlanOverride {
     int draft_tail_split;    // 1: one row runs norm_quant + the LM head, not the fused tail
     int device_cus;          // > 0: persistent grids sized as if the device had this many CUs
     int gemm;                // 0 auto; otherwise a compute-regime kernel variant (lmhead_gemm.hip)
+    int norm_quant;          // 0 a workgroup per row; 1 a wavefront per row (H <= 8192)
 };
 const PlanOverride& plan_override();
 

@@ -202,6 +202,9 @@ mtpd_status mtpd_set_plan_override(const char* key, const char* value) {
     } else if (!strcmp(key, "draft_tail")) {
         ok = clear || !strcmp(value, "split");
         p.draft_tail_split = clear ? 0 : 1;
+    } else if (!strcmp(key, "norm_quant")) {
+        ok = clear || !strcmp(value, "wave") || !strcmp(value, "workgroup");
+        p.norm_quant = !clear && !strcmp(value, "wave") ? 1 : 0;
     } else if (!strcmp(key, "device_cus")) {
         int v = 0;
         ok = clear || parse_ints(value, &v, 1);
@@ -260,8 +263,12 @@ const char* mtpd_draft_tail_plan(int64_t M, int64_t V, int64_t H) {
     }
     char lm[160];
     mtpd::describe_lmhead(M, V, H, lm, sizeof lm);
-    snprintf(buf, sizeof buf, "norm_quant_kernel<%lld> grid=%lldx256 + %s", (long long)((H + 2047) / 2048),
-             (long long)M, lm);
+    if (mtpd::plan_override().norm_quant == 1 && H <= 8192)
+        snprintf(buf, sizeof buf, "norm_quant_wave_kernel<%lld> grid=%lldx256 + %s", (long long)((H + 511) / 512),
+                 (long long)((M + 3) / 4), lm);
+    else
+        snprintf(buf, sizeof buf, "norm_quant_kernel<%lld> grid=%lldx256 + %s", (long long)((H + 2047) / 2048),
+                 (long long)M, lm);
     return buf;
 }
 

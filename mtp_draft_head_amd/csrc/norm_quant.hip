@@ -121,6 +121,80 @@ __global__ __launch_bounds__(256) void norm_quant_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// The same step with one wavefront per row (four rows per 256-thread
+// workgroup), for measurement against the workgroup per row above (plan
+// override "norm_quant" = "wave").  Lane l owns columns k * 512 + 8l .. + 7
+// of each 512-column step (H <= 8192: at most 16 steps in registers);
+// sixteen lanes still cover one 128-column scale block.  The row's sum of
+// squares is the per-lane fp32 sum and one wave sum, with no exchange
+// between waves, so its association differs from the kernel above: results
+// agree with it to rounding, not bit for bit.
+// ---------------------------------------------------------------------------
+
+template <int NSTEP>
+__global__ __launch_bounds__(256) void norm_quant_wave_kernel(
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ residual,
+    const float* __restrict__ gamma, float eps, int H, int M,
+    uint16_t* __restrict__ out_hidden, uint8_t* __restrict__ codes, float* __restrict__ scales)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (row >= M) return;   // the whole wave: nothing below synchronizes across waves
+    const size_t base = (size_t)row * (size_t)H;
+    const int KB = H >> 7;
+
+    float s[NSTEP][8];
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+        const int c = k * 512 + lane * 8;
+        if (c < H) {
+            const uint4 hv = *reinterpret_cast<const uint4*>(hidden + base + c);
+            const uint4 rv = *reinterpret_cast<const uint4*>(residual + base + c);
+            s[k][0] = bf16_lo(hv.x) + bf16_lo(rv.x);
+            s[k][1] = bf16_hi(hv.x) + bf16_hi(rv.x);
+            s[k][2] = bf16_lo(hv.y) + bf16_lo(rv.y);
+            s[k][3] = bf16_hi(hv.y) + bf16_hi(rv.y);
+            s[k][4] = bf16_lo(hv.z) + bf16_lo(rv.z);
+            s[k][5] = bf16_hi(hv.z) + bf16_hi(rv.z);
+            s[k][6] = bf16_lo(hv.w) + bf16_lo(rv.w);
+            s[k][7] = bf16_hi(hv.w) + bf16_hi(rv.w);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s[k][i] = 0.f;
+        }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf(s[k][i], s[k][i], ss);
+    ss = wave_sum_f32(ss);
+    const float rstd = (float)(1.0 / sqrt((double)ss / (double)H + (double)eps));
+    // y over s in place (columns past H hold s = 0 and read a clamped norm
+    // weight; they fill whole 128-column blocks, which are not stored)
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+        const int c = min(k * 512 + lane * 8, H - 8);
+        const float4 g0 = *reinterpret_cast<const float4*>(gamma + c);
+        const float4 g1 = *reinterpret_cast<const float4*>(gamma + c + 4);
+        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[k][i] = (s[k][i] * rstd) * g[i];
+    }
+    float scale[NSTEP];
+    uint2 code[NSTEP];
+    quant_groups<NSTEP>(s, scale, code);
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+        const int c = k * 512 + lane * 8;
+        if (c >= H) continue;   // uniform over each 16-lane scale block
+        *reinterpret_cast<uint4*>(out_hidden + base + c) = pack_bf16x8(s[k]);
+        *reinterpret_cast<uint2*>(codes + base + c) = code[k];
+        if ((lane & 15) == 0) scales[(size_t)row * KB + (c >> 7)] = scale[k];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // The same step with the MTP layer's trailing all-reduce folded in: the norm
 // input is the sum of P row-parallel partial outputs plus the residual
 // ("[Spec Decode][Perf] Fuse the MTP trailing all-reduce; local-argmax draft
@@ -185,6 +259,25 @@ hipError_t launch_norm_quant(const uint16_t* hidden, const uint16_t* residual, c
                              float eps, int64_t M, int64_t H, uint16_t* out_hidden, uint8_t* codes,
                              float* scales, hipStream_t stream)
 {
+    if (plan_override().norm_quant == 1 && H <= 8192) {
+        const int nw = (int)((H + 511) / 512);
+        const dim3 grid((unsigned)((M + 3) / 4)), block(256);
+#define MTPD_NQW_CASE(N)                                                                                   \
+    case N:                                                                                                \
+        hipLaunchKernelGGL(norm_quant_wave_kernel<N>, grid, block, 0, stream, hidden, residual, gamma, eps, \
+                           (int)H, (int)M, out_hidden, codes, scales);                                     \
+        break;
+        switch (nw) {
+            MTPD_NQW_CASE(1) MTPD_NQW_CASE(2) MTPD_NQW_CASE(3) MTPD_NQW_CASE(4)
+            MTPD_NQW_CASE(5) MTPD_NQW_CASE(6) MTPD_NQW_CASE(7) MTPD_NQW_CASE(8)
+            MTPD_NQW_CASE(9) MTPD_NQW_CASE(10) MTPD_NQW_CASE(11) MTPD_NQW_CASE(12)
+            MTPD_NQW_CASE(13) MTPD_NQW_CASE(14) MTPD_NQW_CASE(15) MTPD_NQW_CASE(16)
+            default:
+                return hipErrorInvalidValue;
+        }
+#undef MTPD_NQW_CASE
+        return hipGetLastError();
+    }
     const int nstep = (int)((H + 2047) / 2048);
     const dim3 grid((unsigned)M), block(256);
 #define MTPD_NQ_CASE(N)                                                                              \

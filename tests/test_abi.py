@@ -243,7 +243,8 @@ def test_plan_override_parsing(L):
     auto = L.mtpd_lmhead_plan(24, 2048, 1536).decode()
     for key, bad in [(b"nonsense", b"1"), (b"lmhead_kernel", b"fast"), (b"lmhead_tile", b"2,2"),
                      (b"lmhead_tile", b"2,x,4"), (b"lmhead_stream", b"0,4"), (b"lmhead_kouter", b"1,2,3"),
-                     (b"draft_tail", b"fused"), (b"device_cus", b"-3"), (b"lmhead_rows", b"1,2,3,4")]:
+                     (b"draft_tail", b"fused"), (b"device_cus", b"-3"), (b"lmhead_rows", b"1,2,3,4"),
+                     (b"norm_quant", b"warp")]:
         L.mtpd_clear_error()
         assert L.mtpd_set_plan_override(key, bad) == SHAPE, (key, bad)
         assert L.mtpd_last_error().decode().startswith("MTPD_ERR_SHAPE")
@@ -256,6 +257,11 @@ def test_plan_override_parsing(L):
         assert L.mtpd_lmhead_plan(24, 2048, 1536).decode().startswith("lmhead_argmax_kernel<")
         assert L.mtpd_set_plan_override(b"draft_tail", b"split") == OK
         assert L.mtpd_draft_tail_plan(1, 2048, 1024).decode().startswith("norm_quant_kernel")
+        assert L.mtpd_set_plan_override(b"norm_quant", b"wave") == OK
+        assert L.mtpd_draft_tail_plan(9, 2048, 1024).decode().startswith("norm_quant_wave_kernel<2> grid=3x256")
+        assert L.mtpd_draft_tail_plan(9, 2048, 16384).decode().startswith("norm_quant_kernel<8> grid=9x256")
+        assert L.mtpd_set_plan_override(b"norm_quant", b"workgroup") == OK
+        assert L.mtpd_draft_tail_plan(9, 2048, 1024).decode().startswith("norm_quant_kernel<1> grid=9x256")
     finally:
         assert L.mtpd_set_plan_override(None, None) == OK
     assert L.mtpd_lmhead_plan(24, 2048, 1536).decode() == auto

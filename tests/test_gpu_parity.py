@@ -145,6 +145,23 @@ def test_norm_quant_entry_point_matches_draft_tail():
     assert torch.equal(m, b[3]) and torch.equal(i, b[4])
 
 
+@pytest.mark.parametrize("M,H", [(1, 128), (3, 640), (9, 1024), (64, 6144), (67, 7168), (33, 8192), (320, 7168)])
+def test_norm_quant_wavefront_per_row(M, H):
+    """The wavefront-per-row norm_quant (a plan override, kept to measure the
+    launch shape) meets the oracle to the same tolerances as the
+    workgroup-per-row kernel, ragged row counts and an all-zero row included,
+    and its packing is self-consistent."""
+    d = inputs.random_case(41 + M, M, H, 256, outliers=True, zero_rows=(0,) if M > 2 else ())
+    h, r, g, _, _ = to_dev(d)
+    with mtpd.plan_override(norm_quant="wave"):
+        assert mtpd.draft_tail_plan(max(M, 2), 256, H).startswith("norm_quant_wave_kernel")
+        out_h, codes, scales = mtpd.norm_quant(h, r, g, d["eps"])
+    torch.cuda.synchronize()
+    r1, r2, r3 = check_norm_quant(d, out_h, codes, scales)
+    say(f"  wave per row M={M} H={H}: bf16 {r1}  codes {r2}  scales {r3}")
+    check_self_consistent(codes, scales)
+
+
 @pytest.mark.parametrize("n_idx,cus", [(7, None), (24, None), (40, 8), (64, 8), (100, None)])
 def test_row_index_gather(n_idx, cus):
     """Gathered rows (repeats included) give the same pairs as the ungathered
