@@ -280,6 +280,42 @@ def combine_shards(local_max, local_idx, offsets):
     return out_max, out_idx
 
 
+def combine_topk_shards(local_val, local_idx, offsets, k: int):
+    """Combine per-shard local top-k lists into the global top-k.
+
+    Under vocab parallelism each shard returns, per row, its own largest
+    logits with local indices; the global top-k is taken from those lists
+    rather than from gathered full-vocab logits ("[Spec Decode][Perf] Fuse
+    the MTP trailing all-reduce; local-argmax draft tokens", Summary; the
+    top-8 and top-32 sets are what "feat(glm52): add checkpoint-native MTP
+    speculative decoding", Accuracy, compares).
+
+    local_val, local_idx: [n_shards, n_rows, kk] (any order within a list);
+    offsets: [n_shards] first global vocab row of each shard.  For each row:
+    the k pairs of largest value over all shards' pairs, in descending
+    value, equal values (+0 == -0) by ascending global index; -0 is returned
+    as +0.  Returns (values float32 [n_rows, k], indices int64 [n_rows, k]).
+    """
+    local_val = np.asarray(local_val, np.float32)
+    local_idx = np.asarray(local_idx, np.int64)
+    n_shards, n_rows, kk = local_val.shape
+    if not 1 <= k <= n_shards * kk:
+        raise ValueError("k must lie in [1, n_shards * list length]")
+    out_val = np.empty((n_rows, k), np.float32)
+    out_idx = np.empty((n_rows, k), np.int64)
+    for i in range(n_rows):
+        pairs = []
+        for s in range(n_shards):
+            for j in range(kk):
+                v = float(local_val[s, i, j]) + 0.0   # -0 and +0 compare and sort as one value
+                pairs.append((-v, int(offsets[s]) + int(local_idx[s, i, j])))
+        pairs.sort()
+        for e in range(k):
+            out_val[i, e] = -pairs[e][0] + 0.0
+            out_idx[i, e] = pairs[e][1]
+    return out_val, out_idx
+
+
 def argmax_sharded(codes, scales, w_codes, w_scales, shard_rows, rows=None):
     """Argmax over a vocab split into shards of ``shard_rows`` vocab rows each.
 

@@ -200,3 +200,44 @@ def test_topk_of_a_zero_row_is_the_lowest_indices():
     a[1] = 0; sa[1] = 0
     v, i = oracle.topk(a, sa, w, sw, 8)
     assert list(i[1]) == list(range(8)) and np.all(v[1] == 0)
+
+
+# --------------------------------------------------------------------------
+# vocab-shard combine of top-k lists
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k,shard", [(1, 128), (8, 128), (8, 256), (32, 256)])
+def test_combined_shard_topk_equals_full_vocab_topk(k, shard):
+    """The k largest of the union of per-shard top-k lists are the k largest
+    overall: shards of the oracle's own top-k, combined, equal its full-vocab
+    top-k (values and indices)."""
+    a, sa, w, sw = small_case(60 + k + shard, 4, 384, 1024)
+    full_v, full_i = oracle.topk(a, sa, w, sw, k)
+    vals, idxs, offs = [], [], []
+    for o in range(0, 1024, shard):
+        v, i = oracle.topk(a, sa, w[o:o + shard], sw[o // 128:(o + shard) // 128], k)
+        vals.append(v)
+        idxs.append(i)
+        offs.append(o)
+    cv, ci = oracle.combine_topk_shards(np.stack(vals), np.stack(idxs), offs, k)
+    assert np.array_equal(ci, full_i) and np.array_equal(cv, full_v)
+
+
+def test_combined_topk_of_one_is_the_argmax_combine():
+    rng = np.random.default_rng(3)
+    lv = rng.integers(-4, 4, (5, 7, 1)).astype(np.float32)
+    li = rng.integers(0, 128, (5, 7, 1))
+    offs = [0, 128, 256, 384, 512]
+    cv, ci = oracle.combine_topk_shards(lv, li, offs, 1)
+    m, i = oracle.combine_shards(lv[:, :, 0], li[:, :, 0], offs)
+    assert np.array_equal(ci[:, 0], i) and np.array_equal(cv[:, 0], m)
+
+
+def test_combined_topk_cross_shard_ties_and_signed_zeros():
+    """Hand-built lists: equal values in different shards come out by global
+    index; -0 and +0 are one value (returned as +0)."""
+    lv = np.array([[[3.0, 1.0, -0.0]], [[3.0, 0.0, -2.0]]], np.float32)
+    li = np.array([[[9, 4, 2]], [[1, 0, 5]]])
+    cv, ci = oracle.combine_topk_shards(lv, li, [0, 100], 5)
+    assert list(ci[0]) == [9, 101, 4, 2, 100]
+    assert list(cv[0]) == [3.0, 3.0, 1.0, 0.0, 0.0] and not np.signbit(cv[0, 3])
