@@ -218,6 +218,34 @@ mtpd_status mtpd_argmax_combine(const float *local_max, const int32_t *local_idx
                                 float *out_max, int32_t *out_idx, void *stream);
 
 /*
+ * Vocab-parallel combine of per-shard top-k lists (the same passages as
+ * mtpd_argmax_combine; "feat(glm52): add checkpoint-native MTP speculative
+ * decoding", Accuracy, compares top-8 and top-32 sets).  Shard s covers
+ * global vocab rows shard_offset[s] .. and returned, per row i, its list
+ * (local_val[s][i][0..k), local_idx[s][i][0..k)) from mtpd_fp8_lmhead_topk:
+ * descending values, equal values in ascending index order.  For each row:
+ *   out_idx[i][0..k) = the global indices shard_offset[s] + local_idx[s][i][j]
+ *                      of the k largest values over all shards' lists, in
+ *                      descending value, equal values (+0 and -0 equal) in
+ *                      ascending global index;
+ *   out_val[i][e]    = that value (-0 returned as +0).
+ * When the shards tile [0, V), hold disjoint vocab rows and each returned its
+ * own top-k, this equals the full-vocab top-k.  The lists must be sorted as
+ * described (the combine merges them; unsorted lists give a wrong result,
+ * not an error).
+ *
+ * local_val: [n_shards][n_rows][k] f32, local_idx: [n_shards][n_rows][k]
+ * int32, device memory, row-major.  shard_offset: HOST array of n_shards
+ * values in [0, 2^31 - 128]; every offset + local index must stay below
+ * 2^31 (not checked on the device).  out_val, out_idx: [n_rows][k].
+ * 1 <= n_shards <= 64, 1 <= k <= 32; n_rows == 0 launches nothing.  No
+ * workspace.
+ */
+mtpd_status mtpd_topk_combine(const float *local_val, const int32_t *local_idx,
+                              const int64_t *shard_offset, int64_t n_shards, int64_t n_rows,
+                              int64_t k, float *out_val, int32_t *out_idx, void *stream);
+
+/*
  * Block-scaled FP8 LM head fused with a greedy local top-k
  * ("Reuse packed FP8 logits inputs", Purpose and Dependencies, for the
  * logits; "feat(glm52): add checkpoint-native MTP speculative decoding",

@@ -24,6 +24,8 @@ Entry points (same names as the C ABI):
       -> (max f32 [n], global idx int32 [n]) from per-shard pairs [P, n]
   fp8_lmhead_topk(codes, scales, w_codes, w_scales, k, row_index=None)
       -> (values f32 [n, k], idx int32 [n, k]), descending
+  topk_combine(local_val, local_idx, shard_offsets)
+      -> (values f32 [n, k], global idx int32 [n, k]) from per-shard lists [P, n, k]
 """
 from __future__ import annotations
 
@@ -36,7 +38,8 @@ import torch
 __all__ = [
     "MtpdError", "MtpdLibraryMissing", "norm_quant", "fp8_lmhead_argmax", "draft_tail",
     "workspace_bytes", "Workspace", "library_path", "lib", "lmhead_plan", "draft_tail_plan",
-    "allreduce_norm_quant", "argmax_combine", "fp8_lmhead_topk", "topk_workspace_bytes", "plan_override",
+    "allreduce_norm_quant", "argmax_combine", "topk_combine", "fp8_lmhead_topk", "topk_workspace_bytes",
+    "plan_override",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -100,6 +103,8 @@ def lib():
                                                 ctypes.POINTER(QAct), P]
         L.mtpd_argmax_combine.restype = ctypes.c_int
         L.mtpd_argmax_combine.argtypes = [P, P, ctypes.POINTER(ctypes.c_int64), I64, I64, P, P, P]
+        L.mtpd_topk_combine.restype = ctypes.c_int
+        L.mtpd_topk_combine.argtypes = [P, P, ctypes.POINTER(ctypes.c_int64), I64, I64, I64, P, P, P]
         L.mtpd_fp8_lmhead_topk.restype = ctypes.c_int
         L.mtpd_fp8_lmhead_topk.argtypes = [ctypes.POINTER(QAct), P, I64, ctypes.POINTER(FP8Weight), I64, P, P, P,
                                            ctypes.c_size_t, P]
@@ -403,6 +408,35 @@ def argmax_combine(local_max, local_idx, shard_offsets, out=None):
         _check(lib().mtpd_argmax_combine(local_max.data_ptr(), local_idx.data_ptr(), arr, P, n,
                                          out_max.data_ptr(), out_idx.data_ptr(), _stream(dev)))
     return out_max, out_idx
+
+
+def topk_combine(local_val, local_idx, shard_offsets, out=None):
+    """Global top-k from per-shard top-k lists.
+
+    local_val float32 [P, n, k], local_idx int32 [P, n, k] (device), each list
+    as fp8_lmhead_topk returns it (descending, equal values in index order);
+    shard_offsets: P ints, the first global vocab row of each shard.  Returns
+    (values float32 [n, k], idx int32 [n, k]) with global indices.
+    """
+    _dev(local_val, "local_val", (torch.float32,), 3)
+    _dev(local_idx, "local_idx", (torch.int32,), 3)
+    if local_val.shape != local_idx.shape:
+        raise ValueError("local_val and local_idx differ in shape")
+    P, n, k = local_val.shape
+    offs = [int(o) for o in shard_offsets]
+    if len(offs) != P:
+        raise ValueError(f"{len(offs)} shard offsets for {P} shards")
+    dev = local_val.device
+    if out is None:
+        out_val = torch.empty((n, k), dtype=torch.float32, device=dev)
+        out_idx = torch.empty((n, k), dtype=torch.int32, device=dev)
+    else:
+        out_val, out_idx = out
+    arr = (ctypes.c_int64 * max(P, 1))(*offs)
+    with torch.cuda.device(dev):
+        _check(lib().mtpd_topk_combine(local_val.data_ptr(), local_idx.data_ptr(), arr, P, n, k,
+                                       out_val.data_ptr(), out_idx.data_ptr(), _stream(dev)))
+    return out_val, out_idx
 
 
 def topk_workspace_bytes(n_rows: int, V: int, k: int) -> int:

@@ -36,6 +36,11 @@ struct ShardOffsets {
 hipError_t launch_argmax_combine(const float* local_max, const int32_t* local_idx, const ShardOffsets& offs,
                                  int n_shards, int64_t n_rows, float* out_max, int32_t* out_idx,
                                  hipStream_t stream);
+// top-k lists of at most kMaxTopk keys per row and shard (argmax_combine.hip)
+constexpr int kMaxTopk = 32;
+hipError_t launch_topk_combine(const float* local_val, const int32_t* local_idx, const ShardOffsets& offs,
+                               int n_shards, int64_t n_rows, int k, float* out_val, int32_t* out_idx,
+                               hipStream_t stream);
 
 struct LmheadArgs {
     const uint8_t* a_codes;

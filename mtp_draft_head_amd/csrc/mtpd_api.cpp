@@ -238,7 +238,7 @@ const char* mtpd_last_error(void) { return g_err; }
 
 void mtpd_clear_error(void) { g_err[0] = 0; }
 
-int mtpd_abi_version(void) { return 6; }
+int mtpd_abi_version(void) { return 7; }
 
 const char* mtpd_lmhead_plan(int64_t n_rows, int64_t V, int64_t H) {
     thread_local char buf[160];
@@ -465,6 +465,35 @@ mtpd_status mtpd_argmax_combine(const float* local_max, const int32_t* local_idx
     return hip_status(mtpd::launch_argmax_combine(local_max, local_idx, offs, (int)n_shards, n_rows, out_max, out_idx,
                                                   (hipStream_t)stream),
                       "argmax_combine launch");
+}
+
+mtpd_status mtpd_topk_combine(const float* local_val, const int32_t* local_idx, const int64_t* shard_offset,
+                              int64_t n_shards, int64_t n_rows, int64_t k, float* out_val, int32_t* out_idx,
+                              void* stream) {
+    if (n_shards < 1 || n_shards > mtpd::kMaxShards)
+        return fail(MTPD_ERR_SHAPE, "n_shards=%lld out of [1, %d]", (long long)n_shards, mtpd::kMaxShards);
+    if (n_rows < 0 || n_rows > kMaxRows) return fail(MTPD_ERR_SHAPE, "n_rows=%lld out of [0, 2^24]", (long long)n_rows);
+    if (k < 1 || k > mtpd::kMaxTopk) return fail(MTPD_ERR_SHAPE, "k=%lld out of [1, %d]", (long long)k, mtpd::kMaxTopk);
+    if (!shard_offset) return fail(MTPD_ERR_NULL, "shard_offset is NULL");
+    mtpd::ShardOffsets offs{};
+    for (int64_t s = 0; s < n_shards; ++s) {
+        if (shard_offset[s] < 0 || shard_offset[s] > kMaxV)
+            return fail(MTPD_ERR_SHAPE, "shard_offset[%lld]=%lld out of [0, 2^31-128]", (long long)s,
+                        (long long)shard_offset[s]);
+        offs.off[s] = (uint32_t)shard_offset[s];
+    }
+    if (n_rows == 0) return MTPD_OK;
+    if (!local_val || !local_idx || !out_val || !out_idx) return fail(MTPD_ERR_NULL, "a required pointer is NULL");
+    if (!aligned(local_val, 4) || !aligned(local_idx, 4) || !aligned(out_val, 4) || !aligned(out_idx, 4))
+        return fail(MTPD_ERR_ALIGN, "value/index arrays must be 4-byte aligned");
+    const size_t cand = (size_t)n_shards * (size_t)n_rows * (size_t)k, outn = (size_t)n_rows * (size_t)k;
+    const Range outs[] = {{out_val, outn * 4, "out_val"}, {out_idx, outn * 4, "out_idx"}};
+    const Range ins[] = {{local_val, cand * 4, "local_val"}, {local_idx, cand * 4, "local_idx"}};
+    mtpd_status st = check_alias(outs, 2, ins, 2);
+    if (st != MTPD_OK) return st;
+    return hip_status(mtpd::launch_topk_combine(local_val, local_idx, offs, (int)n_shards, n_rows, (int)k, out_val,
+                                                out_idx, (hipStream_t)stream),
+                      "topk_combine launch");
 }
 
 size_t mtpd_topk_workspace_bytes(int64_t n_rows, int64_t V, int64_t k) {

@@ -117,6 +117,15 @@ int main() {
     CHECK(mtpd_argmax_combine(omax, oidx, offs, 3, 0, at<float>(57344), at<int32_t>(57856), nullptr) == MTPD_OK);
 
     for (int64_t k : {INT64_C(0), INT64_C(33), INT64_C(-1), INT64_MAX})
+        CHECK(mtpd_topk_combine(omax, oidx, offs, 3, M, k, at<float>(57344), at<int32_t>(57856), nullptr) ==
+              MTPD_ERR_SHAPE);
+    CHECK(mtpd_topk_combine(omax, oidx, offs, 65, M, 8, at<float>(57344), at<int32_t>(57856), nullptr) ==
+          MTPD_ERR_SHAPE);
+    CHECK(mtpd_topk_combine(omax, oidx, nullptr, 3, M, 8, at<float>(57344), at<int32_t>(57856), nullptr) ==
+          MTPD_ERR_NULL);
+    CHECK(mtpd_topk_combine(omax, oidx, offs, 3, 0, 8, at<float>(57344), at<int32_t>(57856), nullptr) == MTPD_OK);
+
+    for (int64_t k : {INT64_C(0), INT64_C(33), INT64_C(-1), INT64_MAX})
         CHECK(mtpd_fp8_lmhead_topk(&qa, nullptr, M, &w, k, omax, oidx, wsp, 4096, nullptr) == MTPD_ERR_SHAPE);
     CHECK(mtpd_fp8_lmhead_topk(&qa, nullptr, 0, &w, 8, omax, oidx, wsp, 4096, nullptr) == MTPD_OK);
 
@@ -129,7 +138,7 @@ int main() {
     (void)mtpd_norm_quant(hid, res, g, 1e-6f, M, 100, oh, &qa, nullptr);
     CHECK(std::strcmp(first, mtpd_last_error()) == 0);
     mtpd_clear_error();
-    CHECK(mtpd_abi_version() == 6);
+    CHECK(mtpd_abi_version() == 7);
     std::printf("abi sanitizer run ok\n");
     return 0;
 }

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(L):
     assert {"mtpd_norm_quant", "mtpd_fp8_lmhead_argmax", "mtpd_draft_tail", "mtpd_workspace_bytes",
             "mtpd_status_name", "mtpd_last_error", "mtpd_clear_error", "mtpd_abi_version",
             "mtpd_lmhead_plan", "mtpd_draft_tail_plan", "mtpd_allreduce_norm_quant",
-            "mtpd_argmax_combine", "mtpd_fp8_lmhead_topk", "mtpd_topk_workspace_bytes",
+            "mtpd_argmax_combine", "mtpd_topk_combine", "mtpd_fp8_lmhead_topk", "mtpd_topk_workspace_bytes",
             "mtpd_set_plan_override"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -47,7 +47,7 @@ def test_status_names_and_version(L):
         "MTPD_OK", "MTPD_ERR_NULL", "MTPD_ERR_SHAPE", "MTPD_ERR_ALIGN", "MTPD_ERR_ALIAS",
         "MTPD_ERR_WORKSPACE", "MTPD_ERR_HIP"]
     assert L.mtpd_status_name(99).decode() == "MTPD_UNKNOWN"
-    assert L.mtpd_abi_version() == 6
+    assert L.mtpd_abi_version() == 7
 
 
 def test_workspace_bytes(L):
@@ -192,6 +192,28 @@ def test_argmax_combine_validation(L):
     assert cb(omax=A + 8) == ALIAS                        # output inside local_max ([2][4] f32)
     assert cb(oidx=A + 0x2008) == ALIAS                   # the two outputs overlap
     assert cb(rows=0, lmax=None, lidx=None, omax=None, oidx=None) == OK
+
+
+def test_topk_combine_validation(L):
+    def cb(offs=(0, 1024), n=None, rows=4, k=8, lval=A, lidx=A + 0x1000, oval=A + 0x2000, oidx=A + 0x3000):
+        n = len(offs) if n is None else n
+        arr = (ctypes.c_int64 * max(1, len(offs)))(*offs) if offs is not None else None
+        L.mtpd_clear_error()
+        return L.mtpd_topk_combine(lval, lidx, arr, n, rows, k, oval, oidx, None)
+    assert cb(n=0) == SHAPE
+    assert cb(offs=list(range(65))) == SHAPE
+    assert cb(offs=(0, -128)) == SHAPE
+    assert cb(offs=(0, 1 << 31)) == SHAPE
+    assert cb(offs=None, n=2) == NULL
+    assert cb(rows=-1) == SHAPE
+    assert cb(rows=(1 << 24) + 1) == SHAPE
+    assert cb(k=0) == SHAPE
+    assert cb(k=33) == SHAPE
+    assert cb(lval=None) == NULL
+    assert cb(oval=A + 0x2002) == ALIGN
+    assert cb(oval=A + 0x80) == ALIAS                      # output inside local_val ([2][4][8] f32)
+    assert cb(oidx=A + 0x2040) == ALIAS                    # the two outputs ([4][8] each) overlap
+    assert cb(rows=0, lval=None, lidx=None, oval=None, oidx=None) == OK
 
 
 def test_topk_workspace_bytes(L):

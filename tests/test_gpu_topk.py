@@ -88,3 +88,71 @@ def test_topk_full_size(name, k, workloads):
     codes, scales, wc, ws = _packed(d)
     gv, gi = mtpd.fp8_lmhead_topk(codes, scales, wc, ws, k)
     say(f"topk {name} k={k}: {_check(codes, scales, d, k, gv, gi)}")
+
+
+# (M, H, V, shards, k): vocab shards of 256, 512, 1024 and 128 rows, k from 1
+# to 32, one and several rows per workgroup
+COMBINE = [(5, 640, 2048, 8, 8), (64, 1152, 4096, 8, 32), (17, 384, 1024, 4, 1), (3, 256, 8192, 64, 4),
+           (9, 512, 1024, 1, 16)]
+
+
+@pytest.mark.parametrize("M,H,V,S,k", COMBINE)
+def test_topk_vocab_shards_combine(M, H, V, S, k):
+    """Per-shard top-k lists (one top-k launch per vocab shard) combined on
+    the device: bit for bit the oracle's combine of the same lists, and the
+    oracle's full-vocab top-k outside near ties."""
+    say(f"topk combine M={M} H={H} V={V} shards={S} k={k}")
+    d = inputs.random_case(90 + M + S, M, H, V, outliers=True)
+    codes, scales, wc, ws = _packed(d)
+    R = V // S
+    vals, idxs = [], []
+    for s in range(S):
+        v, i = mtpd.fp8_lmhead_topk(codes, scales, wc[s * R:(s + 1) * R], ws[s * R // 128:(s + 1) * R // 128], k)
+        vals.append(v)
+        idxs.append(i)
+    lv, li = torch.stack(vals), torch.stack(idxs)
+    offs = [s * R for s in range(S)]
+    gv, gi = mtpd.topk_combine(lv, li, offs)
+    torch.cuda.synchronize()
+    ev, ei = oracle.combine_topk_shards(host(lv), host(li), offs, k)
+    assert np.array_equal(host(gi), ei.astype(np.int32))
+    assert np.array_equal(host(gv), ev) and not np.any(np.signbit(host(gv)) & (host(gv) == 0))
+    say(f"  against the full-vocab oracle: {_check(codes, scales, d, k, gv, gi)}")
+
+
+def test_topk_combine_empty_and_planted_ties():
+    """No rows launches nothing; the tiny workload's planted exact ties, split
+    across two shards, still come out lowest global index first."""
+    e = torch.empty((2, 0, 4), dtype=torch.float32, device=DEV)
+    gv, gi = mtpd.topk_combine(e, e.to(torch.int32), [0, 512])
+    assert gv.shape == (0, 4) and gi.shape == (0, 4)
+    d = inputs.make("tiny")
+    codes, scales, wc, ws = _packed(d)
+    V = wc.shape[0]
+    parts = [mtpd.fp8_lmhead_topk(codes, scales, wc[o:o + V // 2], ws[o // 128:(o + V // 2) // 128], 4)
+             for o in (0, V // 2)]
+    gv, gi = mtpd.topk_combine(torch.stack([p[0] for p in parts]), torch.stack([p[1] for p in parts]), [0, V // 2])
+    full_v, full_i = mtpd.fp8_lmhead_topk(codes, scales, wc, ws, 4)
+    assert torch.equal(gi, full_i) and torch.equal(gv, full_v)
+    hi = host(gi)
+    for row, lo, hi_idx in d["meta"]["ties"]:
+        assert hi[row, 0] == lo and hi[row, 1] == hi_idx, (row, hi[row])
+
+
+@pytest.mark.parametrize("k", [8, 32])
+def test_topk_vocab_shards_full_size(k, workloads):
+    """The c=64 full-vocab head as eight 18944-row shards (one GPU's TP8 share
+    each), their top-k lists combined on the device: the oracle's combine of
+    the same lists bit for bit, and the full-vocab top-k outside near ties."""
+    d = workloads("decode_c64_full")
+    codes, scales, wc, ws = _packed(d)
+    S, R = 8, 18944
+    parts = [mtpd.fp8_lmhead_topk(codes, scales, wc[s * R:(s + 1) * R], ws[s * R // 128:(s + 1) * R // 128], k)
+             for s in range(S)]
+    lv, li = torch.stack([p[0] for p in parts]), torch.stack([p[1] for p in parts])
+    offs = [s * R for s in range(S)]
+    gv, gi = mtpd.topk_combine(lv, li, offs)
+    torch.cuda.synchronize()
+    ev, ei = oracle.combine_topk_shards(host(lv), host(li), offs, k)
+    assert np.array_equal(host(gi), ei.astype(np.int32)) and np.array_equal(host(gv), ev)
+    say(f"topk shards c64 k={k} against the full-vocab oracle: {_check(codes, scales, d, k, gv, gi)}")
