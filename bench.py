@@ -41,7 +41,9 @@ steps next to it under tensor parallelism, on one GPU's share:
   topk           norm_quant, then the LM head's top-k (--topk, default 8)
                  instead of the argmax: the streaming kernel writes sorted
                  per-(tile, wave) candidate lists and a merge launch selects;
-                 roofline on the streaming kernel
+                 roofline on the streaming kernel.  The same top-k as 8
+                 vocab-shard launches merged by one topk_combine launch is
+                 timed too (key topk_vocab_shards)
 
 Prints ONE JSON line.  --gpus above 1 is refused: this build drives one GPU.
 """
@@ -178,15 +180,24 @@ def traffic_from_profile(kernel: str, workload: str, variant: str = "tail"):
 
 
 def _read_counters(path):
-    """rocprofv3 counter-collection CSV -> list of (kernel_name, counter, value) per dispatch."""
+    """rocprofv3 counter-collection CSV -> list of (kernel_name, counter, value,
+    dispatch id, grid size in threads) per dispatch."""
     import csv
 
     rows = []
     with open(path, newline="") as f:
         for r in csv.DictReader(f):
             rows.append((r.get("Kernel_Name", ""), r.get("Counter_Name", ""), float(r.get("Counter_Value", 0) or 0),
-                         r.get("Dispatch_Id", "")))
+                         r.get("Dispatch_Id", ""), int(float(r.get("Grid_Size", 0) or 0))))
     return rows
+
+
+def _plan_grid_threads(plan: str):
+    """Threads of the launch a plan string names ("... grid=GxT ..."), or None."""
+    import re
+
+    m = re.search(r"grid=(\d+)x(\d+)", plan)
+    return int(m.group(1)) * int(m.group(2)) if m else None
 
 
 def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, copy_mib: int, variant: str = "tail") -> int:
@@ -206,10 +217,13 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, copy_mib: int, 
            "algorithmic_bytes_per_launch": alg,
            "calibration_copy_bytes": copy_mib << 20}
     total = 0.0
+    # the roofline launch only (a variant may run the same kernel at other
+    # grid sizes, e.g. per-shard launches beside the full one)
+    gthreads = _plan_grid_threads(plan)
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = [r for r in _read_counters(path) if r[1] == counter]
-        copy = [v for k, c, v, _ in rows if "copy" in k.lower()]
-        lm = [v for k, c, v, _ in rows if kname in k]
+        copy = [v for k, c, v, _, _ in rows if "copy" in k.lower()]
+        lm = [v for k, c, v, _, gs in rows if kname in k and (gthreads is None or gs in (0, gthreads))]
         if not copy or not lm:
             print(f"no copy or {kname} dispatches with {counter} in {path}", file=sys.stderr)
             return 1
@@ -256,8 +270,9 @@ def summarize_mfma(workload: str, csv_path: str, bench_log: str) -> int:
     w = inputs.get(workload)
     kname, _, _, plan, flops_alg = roofline_kernel("tail", w.M, w.H, w.V)
     per = {}
-    for k, c, v, disp in _read_counters(csv_path):
-        if kname in k and c in MFMA_COUNTERS:
+    gthreads = _plan_grid_threads(plan)
+    for k, c, v, disp, gs in _read_counters(csv_path):
+        if kname in k and c in MFMA_COUNTERS and (gthreads is None or gs in (0, gthreads)):
             per.setdefault(disp, {}).setdefault(c, 0.0)
             per[disp][c] += v
     runs = [d for d in per.values() if all(c in d for c in MFMA_COUNTERS)]
@@ -558,6 +573,30 @@ def main() -> int:
         def kernel_step(i):
             mtpd.fp8_lmhead_topk(out[1], out[2], wcs[i % n_copies], wss[i % n_copies], TOPK_K, workspace=tk_ws,
                                  out=tk_out)
+
+        # the same top-k as N_SHARDS vocab-shard launches whose lists one
+        # topk_combine launch merges (one GPU's share of each shard, timed as a step)
+        tk_shards = V % (N_SHARDS * 128) == 0
+        if tk_shards:
+            S = V // N_SHARDS
+            tk_offs = [k * S for k in range(N_SHARDS)]
+            tk_parts = [[(wcs[c][k * S:(k + 1) * S], wss[c][k * S // 128:(k + 1) * S // 128])
+                         for k in range(N_SHARDS)] for c in range(n_copies)]
+            tk_lv = torch.empty((N_SHARDS, M, TOPK_K), dtype=torch.float32, device=dev)
+            tk_li = torch.empty((N_SHARDS, M, TOPK_K), dtype=torch.int32, device=dev)
+            tk_cout = (torch.empty((M, TOPK_K), dtype=torch.float32, device=dev),
+                       torch.empty((M, TOPK_K), dtype=torch.int32, device=dev))
+            tk_ws_s = mtpd.Workspace(dev, any_stream=True)
+            tk_ws_s.get_bytes(mtpd.topk_workspace_bytes(M, S, TOPK_K))
+
+            def topk_shard_step(i):
+                mtpd.norm_quant(hid, res, g, d["eps"], out=out[:3])
+                for k, (c, sc) in enumerate(tk_parts[i % n_copies]):
+                    mtpd.fp8_lmhead_topk(out[1], out[2], c, sc, TOPK_K, workspace=tk_ws_s, out=(tk_lv[k], tk_li[k]))
+                mtpd.topk_combine(tk_lv, tk_li, tk_offs, out=tk_cout)
+
+            def topk_combine_step(i):
+                mtpd.topk_combine(tk_lv, tk_li, tk_offs, out=tk_cout)
     elif variant == "tail":
         def step(i):
             mtpd.draft_tail(hid, res, g, d["eps"], wcs[i % n_copies], wss[i % n_copies], workspace=wsp, out=out)
@@ -668,6 +707,12 @@ def main() -> int:
         ms_comb, g3 = timed_graph(combine_step)
         del g3
         extra["argmax_combine_us"] = round(ms_comb * 1e3, 3)
+    if variant == "topk" and tk_shards:
+        ms_ts, g3 = timed_graph(topk_shard_step)
+        ms_tc, g4 = timed_graph(topk_combine_step)
+        del g3, g4
+        extra["topk_vocab_shards"] = {"shards": N_SHARDS, "step_us": round(ms_ts * 1e3, 3),
+                                      "topk_combine_us": round(ms_tc * 1e3, 3)}
     if variant == "allreduce_tail":
         ms_lm_alone, g3 = timed_graph(lm_alone)
         del g3

@@ -88,6 +88,33 @@ def test_summarize_pmc_scales_each_counter_by_the_calibration_copy(scratch_root)
     assert out["kernel_hash"] == "hash-of-lmhead_kouter_kernel"
 
 
+def test_summarize_pmc_takes_only_the_roofline_launch_grid(scratch_root):
+    """A variant that runs the same kernel at another grid (per-shard top-k
+    launches beside the full one) does not dilute the per-launch traffic."""
+    kern = "void mtpd::lmhead_stream_rows_kernel<4, 2, 4, 3, true>(unsigned char const*)"
+    copy = "__amd_rocclr_copyBuffer"
+    grid = 256 * 256   # the topk variant's roofline launch at c=64: grid=256x256
+
+    def write(path, counter, rows):
+        with open(path, "w", newline="") as f:
+            wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name",
+                                               "Counter_Value"])
+            wr.writeheader()
+            for i, (k, g, v) in enumerate(rows):
+                wr.writerow({"Dispatch_Id": i, "Kernel_Name": k, "Grid_Size": g, "Counter_Name": counter,
+                             "Counter_Value": v})
+    write(scratch_root / "f.csv", "FETCH_SIZE", [(copy, 4096, 524288.0), (kern, grid, 455000.0),
+                                                 (kern, 148 * 256, 57000.0), (kern, grid, 455000.0)])
+    write(scratch_root / "w.csv", "WRITE_SIZE", [(copy, 4096, 1048576.0), (kern, grid, 100.0),
+                                                 (kern, 148 * 256, 10.0)])
+    assert bench.summarize_pmc("decode_c64_full", str(scratch_root / "f.csv"), str(scratch_root / "w.csv"),
+                               1024, "topk") == 0
+    with open(bench.traffic_path("lmhead_stream_rows_kernel", "decode_c64_full", "topk")) as f:
+        out = json.load(f)
+    assert out["FETCH_SIZE"]["kernel_dispatches"] == 2 and out["WRITE_SIZE"]["kernel_dispatches"] == 1
+    assert out["bytes_per_launch"] == pytest.approx(455000.0 * 1024 * 2.0 + 100.0 * 1024)
+
+
 def test_summarize_pmc_refuses_a_run_without_the_calibration_copy(scratch_root):
     kern = "void mtpd::lmhead_kouter_kernel<4, 2, 4, 5, 5>(unsigned char const*)"
     _counter_csv(scratch_root / "f.csv", [(kern, "FETCH_SIZE", 1.0)])
