@@ -296,7 +296,8 @@ __global__ __launch_bounds__(512) void lmhead_gemm_kernel(
 //    MT = 5 160-row tiles; MT = 10 320-row tiles (257 to 320 rows in one
 //    tile, so each weight tile is copied once).  Row tiles go in groups of
 //    `group_rows`, row fastest inside a group, consecutive ids on one XCD:
-//    with groups of 4 an XCD's 32 workgroups cover 4 row x 8 column tiles.
+//    with groups of 8 (the 256-row tile's default) an XCD's 32 workgroups
+//    cover 8 row x 4 column tiles.
 //  - Staging: per K block both operand tiles go global -> LDS as [row][128
 //    bytes], eight consecutive lanes per row's 128 bytes (a whole cache line
 //    per eight lanes: measured 12.4 against 10.7 TB/s of L2 -> LDS for four
@@ -934,10 +935,14 @@ int gemm_variant(int64_t n_rows, int64_t H, int64_t a_rows) {
     const int64_t c8 = (n_rows + 255) / 256 * (256 + 256) * 10, c5 = (n_rows + 159) / 160 * (160 + 256) * 10;
     const int64_t c10 = (n_rows + 319) / 320 * (320 + 256) * 11;
     if (c10 < c8 && c10 < c5) return 8;
-    // 256-row tiles in groups of 4 row tiles (an XCD's 32 workgroups then
-    // cover 4 row x 8 column tiles): measured on compute_stress, groups of 1,
-    // 2, 4, 8 and 16 took 7.09, 6.74-6.78, 6.56-6.62, 6.62-6.65 and 6.73 ms
-    return c5 < c8 ? 6 : 2;
+    // 256-row tiles in groups of 8 row tiles (an XCD's 32 workgroups then
+    // cover 8 row x 4 column tiles): measured on compute_stress with the
+    // weight fragment as the first MFMA operand, groups of 4, 8 and 16 took
+    // 6.37-6.40, 6.32-6.36 and 6.44-6.45 ms (eight interleaved pairs of 4
+    // and 8 in two calls, 8 faster in every pair); with the activation
+    // fragment first, groups of 1, 2, 4, 8 and 16 had taken 7.09, 6.74-6.78,
+    // 6.56-6.62, 6.62-6.65 and 6.73 ms
+    return c5 < c8 ? 6 : 3;
 }
 
 void describe_gemm(int64_t n_rows, int64_t V, int64_t H, int64_t a_rows, char* buf, size_t len) {
