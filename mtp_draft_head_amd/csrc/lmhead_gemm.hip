@@ -664,8 +664,18 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
     // first fragment reads, and spread further apart they land too late
     // (measured on compute_stress: 6.9-7.1 ms at the block start, 6.5-6.6 ms
     // from the fifth MFMA, 6.7 ms at every second MFMA).
+    // The 320-row tile (40 MFMAs per block, its weight copies from HBM) does
+    // best with one copy after every second MFMA from the fifth on (mtp5_batch
+    // 312-318 against 320-326 us, three interleaved rounds in one call; every
+    // third MFMA 327-330 us, from the third or the ninth 315-324 us).
     constexpr int kCopyStart = 4;
-    static_assert(kCopyStart + NCOPY <= 4 * MT, "every copy is issued inside the block");
+    constexpr int kCopyStride = MT > 8 ? 2 : 1;
+    static_assert(kCopyStart + kCopyStride * (NCOPY - 1) < 4 * MT, "every copy is issued inside the block");
+    // copy number of MFMA n of the block, or -1
+    auto copy_at = [](int n) {
+        const int d = n - kCopyStart;
+        return d >= 0 && d % kCopyStride == 0 && d / kCopyStride < NCOPY ? d / kCopyStride : -1;
+    };
     const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
     auto copy_one = [&](int s, int kb, int c) {
         if (c < AC) {
@@ -866,14 +876,14 @@ __global__ __launch_bounds__(512) void lmhead_gemm2_kernel(
         // stage 0 (kb is even: chunk boundaries fall here)
         if (kb > 0 && kb % C::SC_BLOCKS == 0 && kb + C::SC_BLOCKS < KB) copy_scales(kb / C::SC_BLOCKS + 1);
         compute(0, [&](int n) {
-            if (n >= kCopyStart && n < kCopyStart + NCOPY && kb + 1 < KB) copy_one(1, kb + 1, n - kCopyStart);
+            if (copy_at(n) >= 0 && kb + 1 < KB) copy_one(1, kb + 1, copy_at(n));
         });
         if (kb + 1 < KB) factors(1, kb + 1);
         drain_barrier();
         if (kb + 1 >= KB) break;
         // stage 1
         compute(1, [&](int n) {
-            if (n >= kCopyStart && n < kCopyStart + NCOPY && kb + 2 < KB) copy_one(0, kb + 2, n - kCopyStart);
+            if (copy_at(n) >= 0 && kb + 2 < KB) copy_one(0, kb + 2, copy_at(n));
         });
         if (kb + 2 < KB) factors(0, kb + 2);
         drain_barrier();
