@@ -76,3 +76,24 @@ def test_entry_points_return_typed_statuses(L, M, H, V, p, ws_bytes):
         assert L.mtpd_last_error() == first   # the first failure's detail is kept
     if M == 0 and s1 == 0:
         assert s2 in (0, 1, 2, 3, 4, 5)       # nothing to launch: never a HIP error
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="fake device pointers must never reach a GPU")
+@SETTINGS
+@given(st.integers(min_value=-2, max_value=70), st.integers(min_value=-2, max_value=300),
+       st.integers(min_value=-2, max_value=40),
+       st.lists(st.sampled_from([0, 128, 18944, (1 << 31) - 128, 1 << 31, -128]), min_size=0, max_size=70),
+       st.lists(ptr_choice, min_size=4, max_size=4))
+def test_combine_entry_points_return_typed_statuses(L, S, n, k, offs, p):
+    """Both vocab-shard combines, under random shard counts, row counts, k,
+    host offsets (short arrays included) and pointer choices."""
+    L.mtpd_clear_error()
+    arr = (ctypes.c_int64 * max(S, len(offs), 1))(*(offs + [0] * max(0, S - len(offs))))
+    s1 = L.mtpd_argmax_combine(_ptr(p[0], 1), _ptr(p[1], 2), arr, S, n, _ptr(p[2], 3), _ptr(p[3], 4), None)
+    assert s1 in STATUSES
+    s2 = L.mtpd_topk_combine(_ptr(p[0], 1), _ptr(p[1], 2), arr, S, n, k, _ptr(p[2], 3), _ptr(p[3], 4), None)
+    assert s2 in STATUSES
+    if not 1 <= S <= 64 or not 0 <= n <= (1 << 24):
+        assert s1 == 2 and s2 == 2
+    if not 1 <= k <= 32 and 1 <= S <= 64 and 0 <= n <= (1 << 24):
+        assert s2 == 2
